@@ -1,0 +1,200 @@
+/*
+ * pkv.h -- C ABI of the MI355X (gfx950) paged-KV decode-attention library.
+ *
+ * The operation is the one the FlashInfer `flashinfer.xqa.xqa` reference page
+ * defines (function signature, parameter list and the closing note on
+ * inferred parameters): a short run of query tokens per sequence attends,
+ * for every group of query heads that shares one KV head, over K/V rows
+ * gathered from a paged cache through an int32 page table up to a
+ * per-sequence length.  Softmax attention is exact (no approximation); the
+ * result is written in place into `out`.
+ *
+ * The absorbed multi-head-latent-attention decode of the vLLM
+ * `models/kimi_k3/nvidia/mla` page (MultiHeadLatentAttention: the decode
+ * branch of `_attention`, `forward_mqa` over the latent cache, and
+ * `_v_up_proj`) is the same call at another shape: one KV head whose rows are
+ * `kv_lora_rank + qk_rope_head_dim` wide (576), with V the first
+ * `kv_lora_rank` (512) entries of each cached row.  Pass the same pointer as
+ * `k_cache` and `v_cache` and `head_dim_v < head_dim_qk` to select it.
+ *
+ * Conventions used throughout (each is a reading of the pages; the design
+ * notes list them with their reasons):
+ *   q        [batch, q_seq_len, num_q_heads, head_dim_qk]   q_dtype, dense
+ *            (beam width 1: the xqa page supports only beam width 1)
+ *   k_cache  NHD: [num_pages, page_size, num_kv_heads, head_dim_qk]
+ *            HND: [num_pages, num_kv_heads, page_size, head_dim_qk]
+ *   v_cache  same layout with head_dim_v, or == k_cache (latent cache; V is
+ *            the first head_dim_v entries of each K row)
+ *   page_table [batch, pages_per_seq] int32; K and V share the table
+ *   seq_lens [batch] uint32; token t of sequence b lives in page
+ *            page_table[b][t / page_size], slot t % page_size
+ *   out      [batch, q_seq_len, num_q_heads, head_dim_v] in q_dtype
+ *   sinks    [num_kv_heads, num_q_heads / num_kv_heads] fp32 or NULL
+ *   mask     [batch, q_seq_len, 2 * ceil(q_seq_len / 32)] uint16 or NULL
+ *
+ *   Query head h uses KV head h / G, G = num_q_heads / num_kv_heads.
+ *   Query token i of sequence b sits at position pos = seq_len - q_seq_len + i
+ *   (the draft tokens are the last q_seq_len positions of the sequence).
+ *   Token t is visible to (b, i, h) iff
+ *       t < seq_len,
+ *       window == 0  or  t > pos - window          (the last `window` tokens,
+ *                                                   the query's own included),
+ *       q_seq_len == 1 or mask == NULL or t < seq_len - q_seq_len
+ *                  or bit (t - (seq_len - q_seq_len)) of mask row (b, i) is 1.
+ *   A mask row is read as little-endian 32-bit words, word w being
+ *   row[2w] | row[2w+1] << 16; draft j is bit (j % 32) of word j / 32.
+ *   logit(t) = q_scale * kv_scale / sqrt(head_dim_qk) * dot(q, k_t)
+ *   out = kv_scale * sum_t e^(logit(t) - M) v_t
+ *         / (sum_t e^(logit(t) - M) + [sinks] e^(sink_h - M)),
+ *   sink_h = sinks[h / G][h % G], M the max over logits and sink;
+ *   a query with no visible token gets out = 0.
+ *
+ * Ownership and threading: every pointer is caller-owned device memory
+ * (`dims` and `opts` are host structs).  The decode call never allocates,
+ * frees or synchronises; it enqueues its kernels on `stream` (a
+ * hipStream_t; NULL is the default stream) and returns.  Calls on one
+ * stream serialise; the workspace must not be shared by calls that may run
+ * concurrently.  The error string is thread-local.
+ *
+ * Errors: every check that can be made on the host is made before any
+ * launch; on failure the call returns a non-zero status, enqueues nothing
+ * and leaves a message for pkv_last_error().  Device-resident data (page
+ * ids, sequence lengths) is not read on the host by the decode call: a
+ * page id outside [0, num_pages) makes the tokens it holds invisible and a
+ * seq_len above pages_per_seq * page_size is clamped to it -- inputs that
+ * are outside the contract, which pkv_validate_inputs() reports.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARGUMENT = 1,   /* malformed shapes, NULLs, bad values   */
+  PKV_ERR_UNSUPPORTED = 2,        /* well-formed but not implemented        */
+  PKV_ERR_WORKSPACE_TOO_SMALL = 3,
+  PKV_ERR_HIP = 4,                /* a HIP runtime call failed              */
+  PKV_ERR_DEVICE_DATA = 5         /* pkv_validate_inputs: bad device data   */
+} pkv_status;
+
+/* Element types.  PKV_FP8_E4M3 is the OCP 8-bit E4M3 format ("fn": no
+ * infinities, S.1111.111 is NaN, largest finite 448) -- the
+ * torch.float8_e4m3fn cache dtype named on the xqa page.  A cache stored as
+ * raw uint8 bytes is the same thing (the Kimi-K3 MLA page views its plain
+ * fp8 cache that way). */
+typedef enum { PKV_F16 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
+
+/* Cache layouts of the xqa page's `kv_layout` parameter. */
+typedef enum { PKV_NHD = 0, PKV_HND = 1 } pkv_layout;
+
+/* What the xqa page infers from tensor shapes (its closing note), passed
+ * explicitly because the ABI carries no shapes. */
+typedef struct pkv_dims {
+  int32_t batch;          /* q.shape[0]                                     */
+  int32_t num_q_heads;    /* q.shape[-2]                                    */
+  int32_t head_dim_qk;    /* q.shape[-1]; also the K row width              */
+  int32_t head_dim_v;     /* V row width = out.shape[-1]                    */
+  int32_t pages_per_seq;  /* page_table.shape[-1]; max_seq_len = this*page  */
+  int32_t num_pages;      /* k_cache.shape[0] (physical pages)              */
+  int32_t q_dtype;        /* pkv_dtype: PKV_F16 or PKV_BF16; out dtype too  */
+  int32_t kv_dtype;       /* pkv_dtype: == q_dtype or PKV_FP8_E4M3          */
+  uint64_t workspace_bytes; /* size of the caller's workspace buffer        */
+} pkv_dims;
+
+/* Kernel paths.  PKV_PATH_AUTO lets the planner choose. */
+typedef enum {
+  PKV_PATH_AUTO = 0,
+  PKV_PATH_VALU = 1,      /* vector-ALU dot products, rows < 16             */
+  PKV_PATH_MFMA = 2,      /* matrix-core tiles, up to 16 rows per KV head   */
+  PKV_PATH_MFMA_MLA = 3   /* matrix-core, 64 rows, latent (aliased) cache   */
+} pkv_path;
+
+/* Optional planner overrides (A/B measurement, split-invariance tests).
+ * Zero-initialised means "all automatic". */
+typedef struct pkv_options {
+  int32_t path;           /* pkv_path                                       */
+  int32_t split_pages;    /* pages per split-KV chunk; 0 = planner's choice */
+  int32_t num_cus;        /* compute units to plan for; 0 = query device    */
+  int32_t target_ctas;    /* planner's grid-size goal; 0 = default          */
+} pkv_options;
+
+/* The plan a decode call would use (pkv_query_plan). */
+typedef struct pkv_plan_info {
+  int32_t path;           /* pkv_path actually selected                     */
+  int32_t split_pages;    /* pages per split                                */
+  int32_t max_splits;     /* grid extent over splits                        */
+  int32_t rows;           /* (num_q_heads / num_kv_heads) * q_seq_len       */
+  int32_t ctas_per_split_grid; /* workgroups launched by the split kernel   */
+  int32_t num_cus;
+  uint64_t workspace_bytes;    /* bytes the call needs                      */
+} pkv_plan_info;
+
+/* ABI version (PKV_ABI_VERSION of the built library). */
+int pkv_abi_version(void);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Validates host arguments and reports the plan and workspace size.  Makes
+ * no device call when opts->num_cus > 0.  `dims->workspace_bytes` is
+ * ignored. */
+pkv_status pkv_query_plan(const pkv_dims* dims, int num_kv_heads, int page_size,
+                          int window, int q_seq_len, const pkv_options* opts,
+                          pkv_plan_info* info);
+
+/* Workspace bytes a decode call with these arguments needs (0 on invalid
+ * arguments; pkv_last_error() says why).  The workspace holds the split-KV
+ * partial results (running max, running sum and unnormalised output per
+ * split), the role of the xqa page's `workspace_buffer`. */
+size_t pkv_workspace_size(const pkv_dims* dims, int num_kv_heads, int page_size,
+                          int window, int q_seq_len);
+
+/* The decode call (xqa page: `xqa(q, k_cache, v_cache, page_table, seq_lens,
+ * output, workspace_buffer, semaphores, num_kv_heads, page_size, sinks,
+ * q_scale, kv_scale, sliding_win_size, kv_layout, ..., q_seq_len, mask)`).
+ * `window` is sliding_win_size (0 = off).  `mask` is read only when
+ * q_seq_len > 1.  `workspace` must hold dims->workspace_bytes >=
+ * pkv_workspace_size(...) bytes and be 256-byte aligned.  The xqa page's
+ * `semaphores`, `sm_count`, `enable_pdl` and `rcp_out_scale` have no
+ * counterpart: the split-KV reduction is a second kernel, the CU count is
+ * queried, and the output scale is 1. */
+pkv_status pkv_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* page_table, const uint32_t* seq_lens,
+                           void* out, void* workspace, int num_kv_heads,
+                           int page_size, int layout, const float* sinks,
+                           float q_scale, float kv_scale, int window,
+                           int q_seq_len, const uint16_t* mask, void* stream,
+                           const pkv_dims* dims);
+
+/* As pkv_decode_attn with planner overrides (opts may be NULL). */
+pkv_status pkv_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* page_table, const uint32_t* seq_lens,
+                              void* out, void* workspace, int num_kv_heads,
+                              int page_size, int layout, const float* sinks,
+                              float q_scale, float kv_scale, int window,
+                              int q_seq_len, const uint16_t* mask, void* stream,
+                              const pkv_dims* dims, const pkv_options* opts);
+
+/* Checks the device-resident inputs the decode call trusts: every page id a
+ * visible token needs lies in [0, num_pages) and q_seq_len <= seq_len <=
+ * pages_per_seq * page_size.  Copies seq_lens and page_table to the host and
+ * synchronises `stream` (a testing and debugging aid, not for the hot path).
+ * Returns PKV_ERR_DEVICE_DATA with a message naming the first offending
+ * sequence, or the host-argument status of pkv_decode_attn. */
+pkv_status pkv_validate_inputs(const int32_t* page_table, const uint32_t* seq_lens,
+                               int num_kv_heads, int page_size, int window,
+                               int q_seq_len, void* stream, const pkv_dims* dims);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

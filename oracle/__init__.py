@@ -1,0 +1,147 @@
+"""fp64 CPU oracle for paged-KV decode attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline
+leg may import this package.  The library's decode path never does; the two
+share no code (this wrapper loads ``pkv_oracle.c`` compiled by gcc, with
+``-O2 -fopenmp`` and no fast-math).
+
+The definition it follows, and the readings taken where the pages leave a
+step open, are stated in the header of ``pkv_oracle.c``.  Every function
+here is pinned by ``tests/test_oracle_pins.py`` against things other than
+itself: the format definitions' own values, library conversions, a dense
+brute-force attention on gathered pages, closed forms and invariants.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pkv_oracle.c")
+_LIB = os.path.join(_HERE, "libpkv_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+DTYPE_CODE = {torch.float16: 0, torch.bfloat16: 1, torch.float8_e4m3fn: 2, torch.uint8: 2}
+LAYOUT_CODE = {"NHD": 0, "HND": 1}
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int), ("q_seq_len", ctypes.c_int),
+        ("num_q_heads", ctypes.c_int), ("num_kv_heads", ctypes.c_int),
+        ("head_dim_qk", ctypes.c_int), ("head_dim_v", ctypes.c_int),
+        ("page_size", ctypes.c_int), ("pages_per_seq", ctypes.c_int),
+        ("num_pages", ctypes.c_int), ("q_dtype", ctypes.c_int),
+        ("kv_dtype", ctypes.c_int), ("layout", ctypes.c_int),
+        ("window", ctypes.c_int), ("v_from_k", ctypes.c_int),
+        ("num_threads", ctypes.c_int),
+        ("q_scale", ctypes.c_double), ("kv_scale", ctypes.c_double),
+    ]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (plain C, fp64, OpenMP, no fast-math)."""
+    with _lock:
+        if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            tmp = _LIB + f".tmp{os.getpid()}"
+            subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                            "-Wall", _SRC, "-o", tmp, "-lm"], check=True)
+            os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        for name in ("pkvo_decode_f16", "pkvo_decode_bf16"):
+            getattr(lib, name).restype = ctypes.c_double
+            getattr(lib, name).argtypes = [ctypes.c_uint16]
+        lib.pkvo_decode_e4m3fn.restype = ctypes.c_double
+        lib.pkvo_decode_e4m3fn.argtypes = [ctypes.c_uint8]
+        lib.pkvo_decode.restype = ctypes.c_int
+        lib.pkvo_decode.argtypes = [ctypes.POINTER(_Problem)] + [ctypes.c_void_p] * 8
+        lib.pkvo_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def decode_f16(bits: int) -> float:
+    return _load().pkvo_decode_f16(bits)
+
+
+def decode_bf16(bits: int) -> float:
+    return _load().pkvo_decode_bf16(bits)
+
+
+def decode_e4m3fn(bits: int) -> float:
+    return _load().pkvo_decode_e4m3fn(bits)
+
+
+def max_threads() -> int:
+    return _load().pkvo_max_threads()
+
+
+def _raw(t: torch.Tensor) -> np.ndarray:
+    """Host copy of a tensor's storage bits (no value conversion)."""
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype in (torch.float16, torch.bfloat16):
+        return t.view(torch.int16).numpy()
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return t.view(torch.uint8).numpy()
+    return t.numpy()
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def decode(q, k_cache, v_cache, page_table, seq_lens, *, num_kv_heads, page_size,
+           kv_layout="NHD", sinks=None, q_scale=1.0, kv_scale=1.0, sliding_win_size=0,
+           q_seq_len=1, mask=None, head_dim_v=None, v_from_k=False, num_pages=None,
+           num_threads=0):
+    """Exact attention in fp64.  q: [B, q_seq_len, Hq, Dqk] (or [B, Hq, Dqk]).
+
+    Returns a float64 tensor [B, q_seq_len, Hq, Dv].  ``v_from_k`` takes V as
+    the first ``head_dim_v`` entries of each K row (the latent cache).
+    """
+    B = q.shape[0]
+    Hq, Dqk = q.shape[-2], q.shape[-1]
+    Tq = q_seq_len
+    assert q.numel() == B * Tq * Hq * Dqk, "q does not hold batch*q_seq_len*Hq*Dqk elements"
+    if head_dim_v is None:
+        head_dim_v = Dqk if (v_from_k or v_cache is None) else v_cache.shape[-1]
+    p = _Problem()
+    p.batch, p.q_seq_len, p.num_q_heads, p.num_kv_heads = B, Tq, Hq, num_kv_heads
+    p.head_dim_qk, p.head_dim_v = Dqk, head_dim_v
+    p.page_size, p.pages_per_seq = page_size, page_table.shape[-1]
+    p.num_pages = k_cache.shape[0] if num_pages is None else num_pages
+    p.q_dtype, p.kv_dtype = DTYPE_CODE[q.dtype], DTYPE_CODE[k_cache.dtype]
+    p.layout = LAYOUT_CODE[kv_layout]
+    p.window, p.v_from_k, p.num_threads = sliding_win_size, 1 if v_from_k else 0, num_threads
+    p.q_scale, p.kv_scale = float(q_scale), float(kv_scale)
+
+    qa = _raw(q)
+    ka = _raw(k_cache)
+    va = None if (v_from_k or v_cache is None) else _raw(v_cache)
+    pt = np.ascontiguousarray(page_table.detach().cpu().to(torch.int32).numpy())
+    sl = np.ascontiguousarray(seq_lens.detach().cpu().reshape(-1).to(torch.int64).numpy().astype(np.uint32))
+    sk = None if sinks is None else np.ascontiguousarray(sinks.detach().cpu().to(torch.float32).numpy())
+    mk = None
+    if mask is not None:
+        mk = np.ascontiguousarray(mask.detach().cpu().view(torch.int16).numpy())
+    out = np.zeros((B, Tq, Hq, head_dim_v), dtype=np.float64)
+    rc = _load().pkvo_decode(ctypes.byref(p), _ptr(qa), _ptr(ka), _ptr(va), _ptr(pt), _ptr(sl),
+                             _ptr(sk), _ptr(mk), _ptr(out))
+    if rc < 0:
+        raise ValueError("oracle: malformed problem sizes")
+    if rc > 0:
+        raise ValueError(f"oracle: sequence {rc - 1} needs a page id outside [0, num_pages)")
+    return torch.from_numpy(out)

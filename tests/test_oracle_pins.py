@@ -1,0 +1,437 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+- storage decoders: every code against numpy / torch conversions, plus the
+  values the format definitions fix (tests/golden);
+- whole result: dense brute-force attention on gathered pages, and torch's
+  scaled_dot_product_attention in fp64;
+- closed forms: one visible token, constant V, q = 0, the counting probe,
+  sinks, windows of 1 and >= L;
+- invariants: page permutation, NHD == HND, fp8 == its bf16 image,
+  causal-mask rows == shorter single-token decodes, all-ones mask == no mask;
+- the mask bit order of the reading, from a fixture;
+- page-table hygiene: unused entries are never dereferenced, a visible token
+  with a bad page id is an error.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_attention_pages_amd import synth
+from tests import dense
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def _same(a, b):
+    return (math.isnan(a) and math.isnan(b)) or a == b
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_e4m3fn_golden_values():
+    for code, val in _read_golden("e4m3fn_values.txt"):
+        got = oracle.decode_e4m3fn(int(code, 16))
+        want = float(val)
+        assert _same(got, want), (code, got, want)
+        if want == 0.0:
+            assert math.copysign(1.0, got) == math.copysign(1.0, want)
+
+
+def test_half_golden_values():
+    for fmt, code, val in _read_golden("half_values.txt"):
+        fn = oracle.decode_f16 if fmt == "f16" else oracle.decode_bf16
+        assert _same(fn(int(code, 16)), float(val)), (fmt, code)
+
+
+def test_f16_all_codes_match_numpy():
+    codes = np.arange(65536, dtype=np.uint16)
+    want = codes.view(np.float16).astype(np.float64)
+    got = np.array([oracle.decode_f16(int(c)) for c in codes])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+
+
+def test_bf16_all_codes_match_torch():
+    codes = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    want = codes.view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.decode_bf16(int(c) & 0xFFFF) for c in codes])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+
+
+def test_e4m3fn_all_codes_match_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    want = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.decode_e4m3fn(int(c)) for c in codes])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.nanmax(np.abs(got)) == 448.0
+
+
+# ---------------------------------------------------------------- helpers
+
+def small(name="tiny", **kw):
+    base = dict(
+        tiny=synth.WORKLOADS["tiny"],
+        gqa=synth.WORKLOADS["llama3_8b_gqa"].replace(batch=3, seq_len_range=(1, 300)),
+        fp8=synth.WORKLOADS["fp8_window_sinks"].replace(
+            batch=3, num_q_heads=8, num_kv_heads=2, seq_len_range=(40, 200), window=50),
+        spec=synth.WORKLOADS["spec_decode"].replace(batch=3, seq_len_range=(4, 200)),
+        mla=synth.WORKLOADS["mla"].replace(batch=2, num_q_heads=4, seq_len_range=(1, 150)),
+    )[name]
+    return base.replace(**kw) if kw else base
+
+
+def run_oracle(w, inp, **over):
+    kw = synth.decode_kwargs(w)
+    sinks = over.pop("sinks", inp["sinks"])
+    kw.update(over)
+    return oracle.decode(inp["q"], inp["k_cache"], None if w.v_from_k else inp["v_cache"],
+                         inp["page_table"], inp["seq_lens"], sinks=sinks, mask=inp["mask"],
+                         head_dim_v=w.head_dim_v, v_from_k=w.v_from_k, **kw)
+
+
+def window_visible(W, Tq):
+    def fn(b, i, L):
+        t = torch.arange(L)
+        pos = L - Tq + i
+        return (t > pos - W) if W > 0 else torch.ones(L, dtype=torch.bool)
+    return fn
+
+
+# ---------------------------------------------------------------- whole result
+
+@pytest.mark.parametrize("name", ["tiny", "gqa", "mla"])
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_matches_dense_brute_force(name, layout):
+    w = small(name, kv_layout=layout)
+    inp = synth.make_inputs(w, seed=11)
+    got = run_oracle(w, inp)
+    want = dense.dense_decode(inp, num_kv_heads=w.num_kv_heads, page_size=w.page_size,
+                              kv_layout=layout, q_scale=w.q_scale, kv_scale=w.kv_scale,
+                              v_from_k=w.v_from_k, head_dim_v=w.head_dim_v)
+    assert torch.isfinite(got).all()
+    torch.testing.assert_close(got, want, rtol=0, atol=1e-12)
+
+
+def test_matches_sdpa_fp64():
+    w = small("gqa", kv_layout="NHD", seq_len_range=(64, 64))
+    inp = synth.make_inputs(w, seed=5)
+    got = run_oracle(w, inp)
+    B, Hq, G = w.batch, w.num_q_heads, w.group
+    for b in range(B):
+        L = int(inp["seq_lens_host"][b])
+        K = torch.stack([dense.gather_rows(inp["k_cache"], inp["page_table_host"][b], L,
+                                           w.page_size, h, "NHD") for h in range(w.num_kv_heads)])
+        V = torch.stack([dense.gather_rows(inp["v_cache"], inp["page_table_host"][b], L,
+                                           w.page_size, h, "NHD") for h in range(w.num_kv_heads)])
+        K = K.repeat_interleave(G, dim=0)
+        V = V.repeat_interleave(G, dim=0)
+        q = dense.to_f64(inp["q"][b, 0]).unsqueeze(1)  # [Hq, 1, D]
+        ref = torch.nn.functional.scaled_dot_product_attention(q, K, V)
+        torch.testing.assert_close(got[b, 0], ref[:, 0], rtol=0, atol=1e-12)
+
+
+def test_window_sinks_fp8_match_dense():
+    w = small("fp8")
+    inp = synth.make_inputs(w, seed=3)
+    got = run_oracle(w, inp)
+    want = dense.dense_decode(inp, num_kv_heads=w.num_kv_heads, page_size=w.page_size,
+                              kv_layout=w.kv_layout, q_scale=w.q_scale, kv_scale=w.kv_scale,
+                              visible_fn=window_visible(w.window, 1), sinks=inp["sinks"])
+    torch.testing.assert_close(got, want, rtol=0, atol=1e-12)
+
+
+def _mask_visible(visible_bool, Tq, W=0):
+    def fn(b, i, L):
+        t = torch.arange(L)
+        vis = torch.ones(L, dtype=torch.bool)
+        drafts = t >= L - Tq
+        j = (t - (L - Tq)).clamp(min=0)
+        vis &= ~drafts | visible_bool[b, i][j]
+        if W > 0:
+            vis &= t > (L - Tq + i) - W
+        return vis
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["causal", "random"])
+@pytest.mark.parametrize("W", [0, 37])
+def test_spec_mask_matches_dense(kind, W):
+    w = small("spec", mask=kind, window=W)
+    inp = synth.make_inputs(w, seed=9)
+    got = run_oracle(w, inp)
+    vis_bool = synth.draft_visibility(kind, w.batch, w.q_seq_len, 9)
+    want = dense.dense_decode(inp, num_kv_heads=w.num_kv_heads, page_size=w.page_size,
+                              kv_layout=w.kv_layout, visible_fn=_mask_visible(vis_bool, w.q_seq_len, W))
+    torch.testing.assert_close(got, want, rtol=0, atol=1e-12)
+
+
+def test_mask_with_33_drafts_uses_second_word():
+    # q_seq_len 33: each row has two 32-bit words; draft 32 lives in word 1
+    w = small("spec", q_seq_len=33, num_q_heads=8, num_kv_heads=8, mask="random",
+              seq_len_range=(40, 120))
+    inp = synth.make_inputs(w, seed=4)
+    assert inp["mask"].shape == (w.batch, 33, 4)
+    got = run_oracle(w, inp)
+    vis_bool = synth.draft_visibility("random", w.batch, 33, 4)
+    want = dense.dense_decode(inp, num_kv_heads=w.num_kv_heads, page_size=w.page_size,
+                              kv_layout=w.kv_layout, visible_fn=_mask_visible(vis_bool, 33))
+    torch.testing.assert_close(got, want, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- mask fixture
+
+def test_causal_mask_words_fixture():
+    rows = _read_golden("causal_mask_tq4.txt")
+    m = synth.pack_mask_bits(synth.draft_visibility("causal", 2, 4, 0))
+    assert m.shape == (2, 4, 2) and m.dtype == torch.uint16
+    for r, w0, w1 in rows:
+        assert int(m[1, int(r), 0]) == int(w0) and int(m[1, int(r), 1]) == int(w1)
+
+
+# ---------------------------------------------------------------- closed forms
+
+def _one_seq(w, L, seed=1):
+    return synth.make_inputs(w.replace(batch=1, fixed_seq_lens=(L,), seq_len_range=None,
+                                       num_pages=None), seed=seed)
+
+
+def _v_row(inp, w, t, kvh):
+    row = dense.gather_rows(inp["v_cache"] if not w.v_from_k else inp["k_cache"],
+                            inp["page_table_host"][0], t + 1, w.page_size, kvh, w.kv_layout)[t]
+    return row[: w.head_dim_v]
+
+
+@pytest.mark.parametrize("name", ["tiny", "fp8", "mla"])
+def test_single_token_returns_its_v_row(name):
+    w = small(name, window=0, sinks=False)
+    inp = _one_seq(w, 1)
+    got = run_oracle(w, inp)
+    for h in range(w.num_q_heads):
+        v = w.kv_scale * _v_row(inp, w, 0, h // w.group)
+        torch.testing.assert_close(got[0, 0, h], v, rtol=0, atol=1e-15)
+
+
+def test_single_token_with_sink():
+    w = small("fp8", window=0)
+    inp = _one_seq(w, 1)
+    got = run_oracle(w, inp)
+    q = dense.to_f64(inp["q"])
+    for h in range(w.num_q_heads):
+        kvh, g = divmod(h, w.group)
+        k = dense.gather_rows(inp["k_cache"], inp["page_table_host"][0], 1, w.page_size, kvh,
+                              w.kv_layout)[0]
+        logit = w.q_scale * w.kv_scale / math.sqrt(w.head_dim_qk) * float(q[0, 0, h] @ k)
+        v = w.kv_scale * _v_row(inp, w, 0, kvh)
+        want = v / (1.0 + math.exp(float(inp["sinks"][kvh, g]) - logit))
+        torch.testing.assert_close(got[0, 0, h], want, rtol=1e-13, atol=1e-15)
+
+
+def test_constant_v_returns_v():
+    w = small("gqa")
+    inp = synth.make_inputs(w, seed=2)
+    inp["v_cache"].fill_(1.25)
+    got = run_oracle(w, inp)
+    torch.testing.assert_close(got, torch.full_like(got, 1.25), rtol=0, atol=1e-14)
+
+
+def test_counting_probe_exact():
+    # q = 0 makes every visible token weigh the same; V[t] = onehot(t mod Dv)
+    # turns the output into (visible tokens per residue class) / (visible count).
+    w = small("gqa", kv_layout="NHD", seq_len_range=(100, 300), head_dim_qk=64, head_dim_v=64)
+    inp = synth.make_inputs(w, seed=6)
+    inp["q"].zero_()
+    v = inp["v_cache"]
+    v.zero_()
+    for b in range(w.batch):
+        L = int(inp["seq_lens_host"][b])
+        for t in range(L):
+            v[int(inp["page_table_host"][b, t // w.page_size]), t % w.page_size, :, t % 64] = 1
+    got = run_oracle(w, inp)
+    for b in range(w.batch):
+        L = int(inp["seq_lens_host"][b])
+        counts = torch.bincount(torch.arange(L) % 64, minlength=64).to(torch.float64)
+        torch.testing.assert_close(got[b, 0], (counts / L).expand(w.num_q_heads, 64),
+                                   rtol=0, atol=1e-15)
+
+
+def test_counting_probe_window():
+    w = small("gqa", kv_layout="HND", seq_len_range=(100, 300), head_dim_qk=64,
+              head_dim_v=64, window=70)
+    inp = synth.make_inputs(w, seed=8)
+    inp["q"].zero_()
+    v = inp["v_cache"]
+    v.zero_()
+    for b in range(w.batch):
+        L = int(inp["seq_lens_host"][b])
+        for t in range(L):
+            v[int(inp["page_table_host"][b, t // w.page_size]), :, t % w.page_size, t % 64] = 1
+    got = run_oracle(w, inp)
+    for b in range(w.batch):
+        L = int(inp["seq_lens_host"][b])
+        ts = torch.arange(L - 70, L)
+        counts = torch.bincount(ts % 64, minlength=64).to(torch.float64)
+        torch.testing.assert_close(got[b, 0], (counts / 70).expand(w.num_q_heads, 64),
+                                   rtol=0, atol=1e-15)
+
+
+def test_sink_to_minus_infinity_is_no_sink():
+    w = small("fp8")
+    inp = synth.make_inputs(w, seed=12)
+    a = run_oracle(w, inp, sinks=torch.full_like(inp["sinks"], -1e30))
+    b = run_oracle(w, inp, sinks=None)
+    torch.testing.assert_close(a, b, rtol=0, atol=0)
+
+
+def test_window_ge_len_is_no_window_and_window_1_is_last_token():
+    w = small("gqa", window=0)
+    inp = synth.make_inputs(w, seed=13)
+    base = run_oracle(w, inp)
+    wide = run_oracle(w, inp, sliding_win_size=int(inp["seq_lens_host"].max()))
+    torch.testing.assert_close(wide, base, rtol=0, atol=0)
+    one = run_oracle(w, inp, sliding_win_size=1)
+    for b in range(w.batch):
+        L = int(inp["seq_lens_host"][b])
+        for h in range(w.num_q_heads):
+            row = dense.gather_rows(inp["v_cache"], inp["page_table_host"][b], L, w.page_size,
+                                    h // w.group, w.kv_layout)[L - 1]
+            torch.testing.assert_close(one[b, 0, h], row, rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_page_permutation_invariance():
+    w = small("gqa")
+    inp = synth.make_inputs(w, seed=14)
+    base = run_oracle(w, inp)
+    P = inp["num_pages"]
+    perm = torch.randperm(P, generator=torch.Generator().manual_seed(99))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(P)
+    inp2 = dict(inp)
+    inp2["k_cache"] = inp["k_cache"][perm].contiguous()   # new page p holds old page perm[p]
+    inp2["v_cache"] = inp["v_cache"][perm].contiguous()
+    inp2["page_table"] = inv[inp["page_table"].to(torch.int64)].to(torch.int32)
+    got = run_oracle(w, inp2)
+    assert torch.equal(got, base)
+
+
+def test_nhd_equals_hnd():
+    w = small("gqa", kv_layout="NHD")
+    inp = synth.make_inputs(w, seed=15)
+    a = run_oracle(w, inp)
+    inp2 = dict(inp)
+    inp2["k_cache"] = inp["k_cache"].transpose(1, 2).contiguous()
+    inp2["v_cache"] = inp["v_cache"].transpose(1, 2).contiguous()
+    b = run_oracle(w.replace(kv_layout="HND"), inp2)
+    assert torch.equal(a, b)
+
+
+def test_fp8_equals_its_bf16_image():
+    # every e4m3fn value is exact in bf16, so an fp8 cache and its bf16 copy
+    # must give the same result for the same kv_scale
+    w = small("fp8")
+    inp = synth.make_inputs(w, seed=16)
+    a = run_oracle(w, inp)
+    inp2 = dict(inp)
+    inp2["k_cache"] = inp["k_cache"].to(torch.bfloat16)
+    inp2["v_cache"] = inp["v_cache"].to(torch.bfloat16)
+    b = run_oracle(w.replace(kv_dtype=torch.bfloat16), inp2)
+    assert torch.equal(a, b)
+
+
+def test_causal_row_equals_shorter_single_token_decode():
+    w = small("spec", mask="causal")
+    inp = synth.make_inputs(w, seed=17)
+    got = run_oracle(w, inp)
+    Tq = w.q_seq_len
+    for i in range(Tq):
+        single = dict(inp)
+        single["q"] = inp["q"][:, i:i + 1].contiguous()
+        single["seq_lens"] = (inp["seq_lens_host"] - Tq + i + 1).to(torch.int32)
+        single["mask"] = None
+        ref = run_oracle(w.replace(q_seq_len=1, mask=None), single)
+        torch.testing.assert_close(got[:, i], ref[:, 0], rtol=0, atol=0)
+
+
+def test_all_ones_mask_equals_no_mask():
+    w = small("spec", mask="ones")
+    inp = synth.make_inputs(w, seed=18)
+    a = run_oracle(w, inp)
+    inp2 = dict(inp)
+    inp2["mask"] = None
+    b = run_oracle(w, inp2)
+    assert torch.equal(a, b)
+    # and each query token then equals a full-length single-token decode
+    for i in range(w.q_seq_len):
+        single = dict(inp2)
+        single["q"] = inp["q"][:, i:i + 1].contiguous()
+        ref = run_oracle(w.replace(q_seq_len=1), single)
+        torch.testing.assert_close(a[:, i], ref[:, 0], rtol=0, atol=0)
+
+
+def test_unused_table_entries_never_read():
+    w = small("gqa")
+    inp = synth.make_inputs(w, seed=19)
+    base = run_oracle(w, inp)
+    t = inp["page_table"].clone()
+    for b in range(w.batch):
+        need = (int(inp["seq_lens_host"][b]) + w.page_size - 1) // w.page_size
+        t[b, need:] = 10 ** 9          # far outside the cache
+    inp2 = dict(inp)
+    inp2["page_table"] = t
+    assert torch.equal(run_oracle(w, inp2), base)
+
+
+def test_visible_bad_page_is_an_error():
+    w = small("gqa")
+    inp = synth.make_inputs(w, seed=20)
+    inp2 = dict(inp)
+    t = inp["page_table"].clone()
+    t[1, 0] = -5
+    inp2["page_table"] = t
+    with pytest.raises(ValueError, match="sequence 1"):
+        run_oracle(w, inp2)
+
+
+def test_empty_sequence_gives_zeros():
+    w = small("fp8")
+    inp = synth.make_inputs(w, seed=21)
+    inp2 = dict(inp)
+    inp2["seq_lens"] = torch.tensor([0, 5, 0], dtype=torch.int32)
+    got = run_oracle(w, inp2)
+    assert torch.equal(got[0], torch.zeros_like(got[0]))
+    assert torch.equal(got[2], torch.zeros_like(got[2]))
+    assert torch.isfinite(got[1]).all() and got[1].abs().sum() > 0
+
+
+def test_poison_makes_stray_reads_visible():
+    # planting a mistake in the oracle's inputs: a table entry of a visible
+    # page pointed at the NaN poison page must poison that sequence's output
+    w = small("gqa")
+    inp = synth.make_inputs(w, seed=22)
+    inp2 = dict(inp)
+    t = inp["page_table"].clone()
+    t[0, 0] = inp["poison_page"]
+    inp2["page_table"] = t
+    got = run_oracle(w, inp2)
+    assert torch.isnan(got[0]).all()
+    assert torch.isfinite(got[1:]).all()
