@@ -1,0 +1,210 @@
+"""Benchmark: paged GQA decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one decode call (split-KV kernel + combine kernel) over one batch
+of the workload, with every input already resident in HBM.  The default
+workload is the Llama-3-8B-shaped GQA decode (batch 64, 32 query heads on 8
+KV heads, head_dim 128, bf16, HND, 64-token pages, lengths uniform in
+[1024, 8192]).  Caches larger than the 256 MB last-level cache are timed as
+they are; smaller ones rotate through replicas totalling >= 1.5 GB so that
+each call reads cold data.
+
+Reported (one JSON line on stdout):
+  value        effective KV bandwidth, algorithmic KV bytes / wall time per
+               call (GB/s); us_per_call and the fraction of the 8 TB/s HBM
+               peak beside it
+  roofline     the split-KV kernel alone (HIP events on the launch stream
+               around it): algorithmic KV bytes per launch / its mean time,
+               against the HBM peak
+  cpu_baseline the fp64 oracle on a bounded sample of the same batch, on the
+               host cores (a reported baseline, not the target)
+Algorithmic KV bytes = sum over sequences of (tokens some query row can see)
+x num_kv_heads x (head_dim_qk + head_dim_v) x element size; a latent cache
+row serves as K and V and counts once.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
+
+
+def kv_bytes_of(w, L: torch.Tensor) -> int:
+    if w.window > 0:
+        lo = (L - w.q_seq_len + 1 - w.window).clamp(min=0)
+        vis = (L - lo).clamp(min=0)
+    else:
+        vis = L
+    elem = 1 if w.kv_dtype == torch.float8_e4m3fn else 2
+    row = w.head_dim_qk + (0 if w.v_from_k else w.head_dim_v)
+    return int(vis.sum()) * w.num_kv_heads * row * elem
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_8b_gqa")
+    ap.add_argument("--path", default=None, help="auto | valu | mfma | mfma_mla")
+    ap.add_argument("--split-pages", type=int, default=0)
+    ap.add_argument("--target-ctas", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (paged decode "
+              "attention shards over sequences and KV heads with no exchange; see the design "
+              "notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import paged_kv_attention_pages_amd as pkv
+    from paged_kv_attention_pages_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    L = synth.draw_seq_lens(w, 1)
+    kf = (L - w.q_seq_len + 1 - w.window).clamp(min=0) if w.window > 0 else None
+    inp = synth.make_inputs(w, seed=1, device=dev, seq_lens=L, keep_from=kf)
+    cache_bytes = inp["k_cache"].numel() * inp["k_cache"].element_size()
+    if not w.v_from_k:
+        cache_bytes += inp["v_cache"].numel() * inp["v_cache"].element_size()
+    n_rep = max(1, math.ceil(1.5e9 / cache_bytes)) if cache_bytes < 1.0e9 else 1
+    reps = [inp]
+    for _ in range(n_rep - 1):
+        k2 = inp["k_cache"].clone()
+        reps.append(dict(inp, k_cache=k2, v_cache=k2 if w.v_from_k else inp["v_cache"].clone()))
+    kv_bytes = kv_bytes_of(w, L)
+    B = L.numel()
+    out = torch.empty((B, w.q_seq_len, w.num_q_heads, w.head_dim_v), dtype=w.q_dtype, device=dev)
+    plan = pkv.query_plan(batch=B, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                          head_dim_qk=w.head_dim_qk, head_dim_v=w.head_dim_v,
+                          pages_per_seq=inp["page_table"].shape[1], page_size=w.page_size,
+                          q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, window=w.window,
+                          q_seq_len=w.q_seq_len, path=args.path, split_pages=args.split_pages,
+                          target_ctas=args.target_ctas)
+    ws = torch.empty(max(plan["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
+
+    def call(i, ev=None):
+        r = reps[i % n_rep]
+        pkv.decode_attn(r["q"], r["k_cache"], r["v_cache"], r["page_table"], r["seq_lens"], out,
+                        ws, num_kv_heads=w.num_kv_heads, page_size=w.page_size, sinks=r["sinks"],
+                        q_scale=w.q_scale, kv_scale=w.kv_scale, sliding_win_size=w.window,
+                        kv_layout=w.kv_layout, q_seq_len=w.q_seq_len, mask=r["mask"],
+                        head_dim_v=w.head_dim_v, path=args.path, split_pages=args.split_pages,
+                        target_ctas=args.target_ctas, split_event=ev)
+
+    K, W = args.steps, args.warmup
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_m = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    for e in ev_m:  # create the device events before handing their handles over
+        e.record()
+    for i in range(W):
+        call(i)
+    print(f"[bench] {w.name}: warmup done ({W} calls), timing {K}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev_s[i].record()
+        call(i, ev_m[i])
+        ev_e[i].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    call_ms = [ev_s[i].elapsed_time(ev_e[i]) for i in range(K)]
+    split_ms = [ev_s[i].elapsed_time(ev_m[i]) for i in range(K)]
+    comb_ms = [ev_m[i].elapsed_time(ev_e[i]) for i in range(K)]
+    split_mean = statistics.fmean(split_ms)
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = kv_bytes / (split_mean * 1e-3) / 1e9
+    print(f"[bench] {w.name}: {ms_per_step * 1e3:.1f} us/call wall, event median "
+          f"{statistics.median(call_ms) * 1e3:.1f} us (split {split_mean * 1e3:.1f} us, combine "
+          f"{statistics.fmean(comb_ms) * 1e3:.1f} us), {value:.0f} GB/s effective, plan {plan}",
+          file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inp, L, args.cpu_seconds)
+
+    dtype = {torch.bfloat16: "bf16", torch.float16: "f16"}[w.q_dtype]
+    if w.kv_dtype == torch.float8_e4m3fn:
+        dtype += "+fp8kv"
+    rec = {
+        "metric": "effective KV GB/s (% of HBM peak) + us/call, paged GQA decode attention",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "us_per_call_event_median": round(statistics.median(call_ms) * 1e3, 2),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "config": {
+            "workload": w.name, "batch": B, "q_seq_len": w.q_seq_len,
+            "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim_qk": w.head_dim_qk, "head_dim_v": w.head_dim_v,
+            "kv_layout": w.kv_layout, "page_size": w.page_size,
+            "seq_len_range": list(w.seq_len_range) if w.seq_len_range else list(w.fixed_seq_lens),
+            "window": w.window, "kv_dtype": str(w.kv_dtype).replace("torch.", ""),
+            "kv_bytes_per_call": kv_bytes, "cache_replicas": n_rep,
+            "path": pkv.PATH_NAMES.get(plan["path"], plan["path"]),
+            "split_pages": plan["split_pages"], "max_splits": plan["max_splits"],
+        },
+        "roofline": {
+            "kernel": "split-KV decode (" + pkv.PATH_NAMES.get(plan["path"], "?") + ")",
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "launch_us_mean": round(split_mean * 1e3, 2),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(w, inp, L, budget_s):
+    """The oracle (as is) on the first n sequences of the batch, n sized to the budget."""
+    import oracle
+    from paged_kv_attention_pages_amd import synth
+
+    cores = len(os.sched_getaffinity(0))
+    k_host = inp["k_cache"].cpu()
+    v_host = None if w.v_from_k else inp["v_cache"].cpu()
+    kw = dict(head_dim_v=w.head_dim_v, v_from_k=w.v_from_k, num_threads=cores,
+              **synth.decode_kwargs(w))
+    sel = lambda t, n: None if t is None else t[:n].cpu()
+
+    def run(n):
+        t = time.perf_counter()
+        oracle.decode(sel(inp["q"], n), k_host, v_host, sel(inp["page_table"], n),
+                      sel(inp["seq_lens"], n), sinks=None if inp["sinks"] is None else inp["sinks"].cpu(),
+                      mask=sel(inp["mask"], n), **kw)
+        return time.perf_counter() - t
+
+    t1 = run(1)
+    n = int(max(1, min(L.numel(), budget_s / max(t1, 1e-3))))
+    dt = run(n) if n > 1 else t1
+    sample_bytes = kv_bytes_of(w, L[:n])
+    print(f"[bench] oracle: {n} sequences in {dt:.2f} s on {cores} threads", file=sys.stderr,
+          flush=True)
+    return {"value": round(sample_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "ms_per_sequence": round(dt * 1e3 / n, 2),
+            "sample": f"first {n} of {L.numel()} sequences of the same batch (all heads), fp64"}
+
+
+if __name__ == "__main__":
+    main()

@@ -124,6 +124,10 @@ typedef struct pkv_options {
   int32_t split_pages;    /* pages per split-KV chunk; 0 = planner's choice */
   int32_t num_cus;        /* compute units to plan for; 0 = query device    */
   int32_t target_ctas;    /* planner's grid-size goal; 0 = default          */
+  void* split_event;      /* hipEvent_t or NULL: when set, it is recorded on
+                             the call's stream after the split-KV kernel and
+                             before the combine kernel (timing one kernel with
+                             events; no work changes)                       */
 } pkv_options;
 
 /* The plan a decode call would use (pkv_query_plan). */

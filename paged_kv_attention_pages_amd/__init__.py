@@ -1,0 +1,276 @@
+"""Paged-KV decode attention for MI355X (gfx950): Python binding of libpkv.so.
+
+A thin ctypes layer over the C ABI declared in ``include/pkv.h``: it reads
+shapes, dtypes, device pointers and the current HIP stream from torch tensors
+and passes them through.  Every step of the attention runs in the library's
+HIP kernels; there is no Python or CPU fallback, and calling into a missing
+library raises.
+
+``decode_attn`` mirrors the parameters of FlashInfer's ``flashinfer.xqa.xqa``
+(reference page: q, k_cache, v_cache, page_table, seq_lens, output,
+workspace_buffer, num_kv_heads, page_size, sinks, q_scale, kv_scale,
+sliding_win_size, kv_layout, q_seq_len, mask).  The workspace, when not
+given, is cached per device and grown on demand, as the vllm-omni trtllm_attn
+backend page does with its attention workspace (``_get_workspace``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = ["decode_attn", "workspace_size", "query_plan", "validate_inputs", "library_path",
+           "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "PATH_MFMA_MLA", "PkvError"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_MFMA_MLA = 0, 1, 2, 3
+PATH_NAMES = {PATH_VALU: "valu", PATH_MFMA: "mfma", PATH_MFMA_MLA: "mfma_mla"}
+_STATUS = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARGUMENT", 2: "PKV_ERR_UNSUPPORTED",
+           3: "PKV_ERR_WORKSPACE_TOO_SMALL", 4: "PKV_ERR_HIP", 5: "PKV_ERR_DEVICE_DATA"}
+_DTYPE = {torch.float16: 0, torch.bfloat16: 1, torch.float8_e4m3fn: 2, torch.uint8: 2}
+_LAYOUT = {"NHD": 0, "HND": 1}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("split_pages", ctypes.c_int32),
+                ("num_cus", ctypes.c_int32), ("target_ctas", ctypes.c_int32),
+                ("split_event", ctypes.c_void_p)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("split_pages", ctypes.c_int32),
+                ("max_splits", ctypes.c_int32), ("rows", ctypes.c_int32),
+                ("ctas_per_split_grid", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+_vp = ctypes.c_void_p
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded libpkv.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        with _lib_lock:
+            if _lib is None:
+                if not os.path.exists(_LIB_PATH):
+                    raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                                       "`python -m paged_kv_attention_pages_amd.build`")
+                L = ctypes.CDLL(_LIB_PATH)
+                L.pkv_abi_version.restype = ctypes.c_int
+                L.pkv_last_error.restype = ctypes.c_char_p
+                L.pkv_query_plan.restype = ctypes.c_int
+                L.pkv_query_plan.argtypes = [ctypes.POINTER(Dims), ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.POINTER(Options),
+                                             ctypes.POINTER(PlanInfo)]
+                L.pkv_workspace_size.restype = ctypes.c_size_t
+                L.pkv_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_int]
+                dec = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                       _vp, ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _vp,
+                       ctypes.POINTER(Dims)]
+                L.pkv_decode_attn.restype = ctypes.c_int
+                L.pkv_decode_attn.argtypes = dec
+                L.pkv_decode_attn_ex.restype = ctypes.c_int
+                L.pkv_decode_attn_ex.argtypes = dec + [ctypes.POINTER(Options)]
+                L.pkv_validate_inputs.restype = ctypes.c_int
+                L.pkv_validate_inputs.argtypes = [_vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.c_int, _vp, ctypes.POINTER(Dims)]
+                _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise PkvError(status, lib().pkv_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dims(q, k_cache, page_table, head_dim_v, q_seq_len, workspace_bytes=0) -> Dims:
+    d = Dims()
+    d.batch = q.shape[0]
+    d.num_q_heads = q.shape[-2]
+    d.head_dim_qk = q.shape[-1]
+    d.head_dim_v = head_dim_v
+    d.pages_per_seq = page_table.shape[-1]
+    d.num_pages = k_cache.shape[0]
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise PkvError(1, f"q dtype must be float16 or bfloat16, got {q.dtype}")
+    if k_cache.dtype not in _DTYPE:
+        raise PkvError(1, f"unsupported KV cache dtype {k_cache.dtype}")
+    d.q_dtype = _DTYPE[q.dtype]
+    d.kv_dtype = _DTYPE[k_cache.dtype]
+    d.workspace_bytes = workspace_bytes
+    return d
+
+
+def _options(path=None, split_pages=0, num_cus=0, target_ctas=0, split_event=None):
+    if not (path or split_pages or num_cus or target_ctas or split_event):
+        return None
+    o = Options()
+    o.path = {None: 0, "auto": 0, "valu": 1, "mfma": 2, "mfma_mla": 3}.get(path, path)
+    o.split_pages, o.num_cus, o.target_ctas = split_pages, num_cus, target_ctas
+    o.split_event = split_event
+    return o
+
+
+def query_plan(*, batch, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, pages_per_seq,
+               page_size, q_dtype=torch.bfloat16, kv_dtype=None, num_pages=1, window=0,
+               q_seq_len=1, path=None, split_pages=0, num_cus=0, target_ctas=0) -> dict:
+    """The plan the library would use (host only when num_cus > 0)."""
+    d = Dims(batch, num_q_heads, head_dim_qk, head_dim_v, pages_per_seq, num_pages,
+             _DTYPE[q_dtype], _DTYPE[kv_dtype or q_dtype], 0)
+    info = PlanInfo()
+    o = _options(path, split_pages, num_cus, target_ctas)
+    _check(lib().pkv_query_plan(ctypes.byref(d), num_kv_heads, page_size, window, q_seq_len,
+                                None if o is None else ctypes.byref(o), ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in PlanInfo._fields_}
+
+
+def workspace_size(*, batch, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, pages_per_seq,
+                   page_size, q_dtype=torch.bfloat16, kv_dtype=None, window=0, q_seq_len=1) -> int:
+    d = Dims(batch, num_q_heads, head_dim_qk, head_dim_v, pages_per_seq, 1, _DTYPE[q_dtype],
+             _DTYPE[kv_dtype or q_dtype], 0)
+    return lib().pkv_workspace_size(ctypes.byref(d), num_kv_heads, page_size, window, q_seq_len)
+
+
+_ws_cache: dict = {}
+
+
+def _workspace(device, nbytes: int) -> torch.Tensor:
+    ws = _ws_cache.get(device)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[device] = ws
+    return ws
+
+
+def _shape_checks(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size,
+                  kv_layout, q_seq_len, head_dim_v, mask):
+    B, Hq, Dk = q.shape[0], q.shape[-2], q.shape[-1]
+    if q.numel() != B * q_seq_len * Hq * Dk:
+        raise PkvError(1, f"q of shape {tuple(q.shape)} does not hold batch x q_seq_len "
+                          f"({q_seq_len}) x num_q_heads x head_dim elements (beam width 1 only)")
+    if kv_layout not in _LAYOUT:
+        raise PkvError(1, f"kv_layout must be 'NHD' or 'HND', got {kv_layout!r}")
+    if k_cache.dim() != 4:
+        raise PkvError(1, f"k_cache must be 4-D, got shape {tuple(k_cache.shape)}")
+    ps_dim, h_dim = (1, 2) if kv_layout == "NHD" else (2, 1)
+    if k_cache.shape[ps_dim] != page_size or k_cache.shape[h_dim] != num_kv_heads \
+            or k_cache.shape[3] != Dk:
+        raise PkvError(1, f"k_cache shape {tuple(k_cache.shape)} does not match {kv_layout} with "
+                          f"page_size {page_size}, num_kv_heads {num_kv_heads}, head_dim {Dk}")
+    if v_cache is not k_cache and v_cache.data_ptr() != k_cache.data_ptr():
+        if tuple(v_cache.shape[:3]) != tuple(k_cache.shape[:3]) or v_cache.shape[3] != head_dim_v:
+            raise PkvError(1, f"v_cache shape {tuple(v_cache.shape)} does not match k_cache "
+                              f"{tuple(k_cache.shape)} with head_dim_v {head_dim_v}")
+        if v_cache.dtype != k_cache.dtype:
+            raise PkvError(1, "k_cache and v_cache must have the same dtype")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.shape[0] != B:
+        raise PkvError(1, f"page_table must be int32 [batch, pages_per_seq], got "
+                          f"{page_table.dtype} {tuple(page_table.shape)}")
+    if seq_lens.dtype not in (torch.int32, torch.uint32) or seq_lens.numel() != B:
+        raise PkvError(1, f"seq_lens must be uint32 (or int32) [batch] or [batch, 1], got "
+                          f"{seq_lens.dtype} {tuple(seq_lens.shape)}")
+    if output.dtype != q.dtype or output.numel() != B * q_seq_len * Hq * head_dim_v:
+        raise PkvError(1, f"output must have q's dtype and batch x q_seq_len x num_q_heads x "
+                          f"head_dim_v elements, got {output.dtype} {tuple(output.shape)}")
+    if mask is not None and q_seq_len > 1:
+        want = (B, q_seq_len, ((q_seq_len + 31) // 32) * 2)
+        if mask.dtype not in (torch.uint16, torch.int16) or tuple(mask.shape) != want:
+            raise PkvError(1, f"mask must be uint16 {want}, got {mask.dtype} {tuple(mask.shape)}")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("page_table", page_table), ("seq_lens", seq_lens), ("output", output),
+                    ("mask", mask)):
+        if t is not None and not t.is_contiguous():
+            raise PkvError(1, f"{name} must be contiguous")
+        if t is not None and t.device != q.device:
+            raise PkvError(1, f"{name} is on {t.device}, q on {q.device}")
+
+
+def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buffer=None, *,
+                num_kv_heads, page_size, sinks=None, q_scale=1.0, kv_scale=1.0,
+                sliding_win_size=0, kv_layout="NHD", q_seq_len=1, mask=None, head_dim_v=None,
+                path=None, split_pages=0, target_ctas=0, stream=None, split_event=None):
+    """Paged-KV decode attention, written in place into ``output``.
+
+    q [B, q_seq_len, Hq, Dqk] (or [B, Hq, Dqk], or the xqa page's beam-1
+    forms); caches NHD [P, page_size, Hkv, D] or HND [P, Hkv, page_size, D]
+    in q's dtype or float8_e4m3fn (uint8 bytes are read as e4m3fn); pass the
+    same tensor as k_cache and v_cache with head_dim_v < Dqk for a latent
+    (MLA) cache whose rows start with V.  ``split_event`` (a torch.cuda.Event
+    that has been recorded once) is recorded between the split-KV and the
+    combine kernel.  Returns ``output``.
+    """
+    if head_dim_v is None:
+        head_dim_v = output.shape[-1]
+    if q.device.type != "cuda":
+        raise PkvError(1, "decode_attn runs on the GPU only: q must be a device tensor")
+    _shape_checks(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size,
+                  kv_layout, q_seq_len, head_dim_v, mask)
+    if sinks is not None:
+        if sinks.dtype != torch.float32 or sinks.numel() != q.shape[-2] or not sinks.is_contiguous():
+            raise PkvError(1, "sinks must be contiguous float32 [num_kv_heads, head_group_ratio]")
+    L = lib()
+    ev = None if split_event is None else split_event.cuda_event
+    opts = _options(path, split_pages, 0, target_ctas, ev)
+    d = _dims(q, k_cache, page_table, head_dim_v, q_seq_len)
+    if workspace_buffer is None:
+        info = PlanInfo()
+        _check(L.pkv_query_plan(ctypes.byref(d), num_kv_heads, page_size, sliding_win_size,
+                                q_seq_len, None if opts is None else ctypes.byref(opts),
+                                ctypes.byref(info)))
+        workspace_buffer = _workspace(q.device, info.workspace_bytes)
+    d.workspace_bytes = workspace_buffer.numel() * workspace_buffer.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens),
+                _ptr(output), _ptr(workspace_buffer), num_kv_heads, page_size, _LAYOUT[kv_layout],
+                _ptr(sinks), float(q_scale), float(kv_scale), int(sliding_win_size),
+                int(q_seq_len), _ptr(mask if q_seq_len > 1 else None), ctypes.c_void_p(stream),
+                ctypes.byref(d))
+        if opts is None:
+            st = L.pkv_decode_attn(*args)
+        else:
+            st = L.pkv_decode_attn_ex(*args, ctypes.byref(opts))
+    _check(st)
+    return output
+
+
+def validate_inputs(q, k_cache, page_table, seq_lens, *, num_kv_heads, page_size,
+                    sliding_win_size=0, q_seq_len=1, head_dim_v=None, stream=None):
+    """Check the device-resident page ids and lengths (synchronises)."""
+    d = _dims(q, k_cache, page_table, head_dim_v or q.shape[-1], q_seq_len)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib().pkv_validate_inputs(_ptr(page_table), _ptr(seq_lens), num_kv_heads, page_size,
+                                     sliding_win_size, q_seq_len, ctypes.c_void_p(stream),
+                                     ctypes.byref(d)))

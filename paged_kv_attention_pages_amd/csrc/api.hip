@@ -1,0 +1,367 @@
+// api.hip -- the C ABI of include/pkv.h: argument checks, the split-KV
+// planner, workspace layout and kernel launches.
+//
+// Operation: FlashInfer `flashinfer.xqa.xqa` reference page (paged-KV decode
+// attention: parameters q, k_cache, v_cache, page_table, seq_lens, output,
+// workspace_buffer, num_kv_heads, page_size, sinks, q_scale, kv_scale,
+// sliding_win_size, kv_layout, q_seq_len, mask, and the note on the
+// parameters inferred from shapes).  Errors follow the explicit-message style
+// of the vllm-omni trtllm_attn backend page (metadata validation in
+// `forward_cuda`): every malformed argument is rejected with a message, and
+// nothing falls back silently.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/pkv.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int kv_elem(int dt) { return dt == PKV_FP8_E4M3 ? 1 : 2; }
+
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+struct Plan {
+  int path;
+  int rows;
+  int split_pages;
+  int max_splits;
+  int num_cus;
+  size_t ws_o_bytes;   // partial outputs
+  size_t ws_ml_off;    // offset of (max, sum) pairs
+  size_t ws_bytes;
+};
+
+// Host-side checks shared by every entry point, then the plan.
+pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window, int Tq,
+                     bool aliased, const pkv_options* opts, Plan* pl) {
+  if (d == nullptr) return fail(PKV_ERR_INVALID_ARGUMENT, "dims is NULL");
+  if (d->batch < 0) return fail(PKV_ERR_INVALID_ARGUMENT, "batch must be >= 0, got %d", d->batch);
+  if (d->num_q_heads < 1)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "num_q_heads must be >= 1, got %d", d->num_q_heads);
+  if (Hkv < 1) return fail(PKV_ERR_INVALID_ARGUMENT, "num_kv_heads must be >= 1, got %d", Hkv);
+  if (d->num_q_heads % Hkv != 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT,
+                "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", d->num_q_heads, Hkv);
+  if (ps != 16 && ps != 32 && ps != 64 && ps != 128)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "page_size must be one of 16, 32, 64, 128; got %d", ps);
+  if (layout != PKV_NHD && layout != PKV_HND)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "kv_layout must be NHD (0) or HND (1); got %d", layout);
+  if (window < 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "sliding window must be >= 0 (0 = off); got %d", window);
+  if (Tq < 1) return fail(PKV_ERR_INVALID_ARGUMENT, "q_seq_len must be >= 1; got %d", Tq);
+  if (d->pages_per_seq < 1)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "pages_per_seq must be >= 1; got %d", d->pages_per_seq);
+  if (d->num_pages < 1)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "num_pages must be >= 1; got %d", d->num_pages);
+  if (d->head_dim_qk < 1 || d->head_dim_v < 1)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "head dims must be >= 1; got %d / %d", d->head_dim_qk,
+                d->head_dim_v);
+  if (d->q_dtype != PKV_F16 && d->q_dtype != PKV_BF16)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "q dtype must be float16 (0) or bfloat16 (1); got %d",
+                d->q_dtype);
+  if (d->kv_dtype != d->q_dtype && d->kv_dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_INVALID_ARGUMENT,
+                "KV cache dtype must equal the query dtype or be float8_e4m3fn; got %d for q %d",
+                d->kv_dtype, d->q_dtype);
+  if ((int64_t)d->pages_per_seq * ps > INT32_MAX / 2)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "pages_per_seq * page_size too large");
+
+  const int G = d->num_q_heads / Hkv;
+  const int64_t R64 = (int64_t)G * Tq;
+  const int R = (int)(R64 > INT32_MAX ? INT32_MAX : R64);
+  const int Dk = d->head_dim_qk, Dv = d->head_dim_v;
+  const int want = opts ? opts->path : PKV_PATH_AUTO;
+  if (want < PKV_PATH_AUTO || want > PKV_PATH_MFMA_MLA)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "unknown path %d", want);
+
+  const bool std_shape = Dk == Dv && (Dk == 64 || Dk == 128 || Dk == 256) && R <= 16;
+  const bool mla_shape = Dk == 576 && Dv == 512 && aliased && R <= 64 && Tq <= 32 &&
+                         d->kv_dtype != PKV_FP8_E4M3;
+  const bool valu_ok = std_shape && Dk == 128 && R <= 8;
+  int path;
+  if (want == PKV_PATH_AUTO) {
+    if (std_shape) path = PKV_PATH_MFMA;
+    else if (mla_shape) path = PKV_PATH_MFMA_MLA;
+    else if (Dk == 576 && Dv == 512 && !aliased)
+      return fail(PKV_ERR_UNSUPPORTED,
+                  "head dims 576/512 are supported for the latent cache only (v_cache == k_cache)");
+    else
+      return fail(PKV_ERR_UNSUPPORTED,
+                  "unsupported shape: head_dim_qk %d, head_dim_v %d, %d rows per KV head "
+                  "(supported: equal head dims 64/128/256 with <= 16 rows, or the 576/512 "
+                  "latent cache with <= 64 rows, 16-bit cache and q_seq_len <= 32)",
+                  Dk, Dv, R);
+  } else {
+    path = want;
+    if (path == PKV_PATH_MFMA && !std_shape)
+      return fail(PKV_ERR_UNSUPPORTED, "matrix-core path needs equal head dims 64/128/256 and "
+                                       "<= 16 rows per KV head");
+    if (path == PKV_PATH_VALU && !valu_ok)
+      return fail(PKV_ERR_UNSUPPORTED, "vector path needs head_dim 128 and <= 8 rows per KV head");
+    if (path == PKV_PATH_MFMA_MLA && !mla_shape)
+      return fail(PKV_ERR_UNSUPPORTED, "latent path needs head dims 576/512, v_cache == k_cache, "
+                                       "a 16-bit cache, <= 64 rows and q_seq_len <= 32");
+  }
+
+  // ---- split planning: chunks of whole pages; grid sized for the CU count
+  const int cus = (opts && opts->num_cus > 0) ? opts->num_cus : device_cus();
+  const int64_t pps = d->pages_per_seq;
+  int64_t pages_max = pps;
+  if (window > 0) pages_max = std::min<int64_t>(pps, cdiv((int64_t)window + Tq - 1, ps) + 1);
+  const int64_t units = (int64_t)d->batch * Hkv;
+  const int64_t row_bytes = (int64_t)(Dk + (aliased ? 0 : Dv)) * kv_elem(d->kv_dtype);
+  const int64_t page_bytes = (int64_t)ps * row_bytes;
+  const int64_t partial_bytes = (int64_t)R * Dv * 4 + (int64_t)R * 8;
+  // keep each split's partial-result traffic under ~1/8 of its cache bytes,
+  // and every split at least 256 tokens long
+  int64_t min_pages = std::max<int64_t>(cdiv(8 * partial_bytes, page_bytes), cdiv(256, ps));
+  const int64_t target = (opts && opts->target_ctas > 0) ? opts->target_ctas : 16LL * cus;
+  int64_t sp = units > 0 ? cdiv(units * pages_max, target) : pages_max;
+  sp = std::max(sp, min_pages);
+  sp = std::min(sp, pages_max);
+  if (opts && opts->split_pages > 0) sp = std::min<int64_t>(opts->split_pages, pages_max);
+  sp = std::max<int64_t>(sp, 1);
+  const int64_t S = cdiv(pages_max, sp);
+  if (S > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many splits (%lld)", (long long)S);
+
+  pl->path = path;
+  pl->rows = R;
+  pl->split_pages = (int)sp;
+  pl->max_splits = (int)S;
+  pl->num_cus = cus;
+  const size_t nrow = (size_t)d->batch * Hkv * S * R;
+  if (S > 1) {
+    pl->ws_o_bytes = nrow * Dv * sizeof(float);
+    pl->ws_ml_off = (pl->ws_o_bytes + 255) & ~(size_t)255;
+    pl->ws_bytes = pl->ws_ml_off + nrow * 2 * sizeof(float);
+  } else {
+    pl->ws_o_bytes = pl->ws_ml_off = pl->ws_bytes = 0;
+  }
+  return PKV_OK;
+}
+
+bool misaligned(const void* p, size_t a) { return ((uintptr_t)p % a) != 0; }
+
+pkv_status decode(const void* q, const void* k, const void* v, const int32_t* page_table,
+                  const uint32_t* seq_lens, void* out, void* workspace, int Hkv, int ps,
+                  int layout, const float* sinks, float q_scale, float kv_scale, int window,
+                  int Tq, const uint16_t* mask, void* stream, const pkv_dims* d,
+                  const pkv_options* opts) {
+  Plan pl;
+  const bool aliased = v != nullptr && v == k && d != nullptr && d->head_dim_v < d->head_dim_qk;
+  pkv_status st = make_plan(d, Hkv, ps, layout, window, Tq, aliased, opts, &pl);
+  if (st != PKV_OK) return st;
+  if (d->batch == 0) return PKV_OK;
+  if (!q || !k || !v || !page_table || !seq_lens || !out)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache, page_table, seq_lens and out "
+                                          "must not be NULL");
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if (!std::isfinite(q_scale) || !std::isfinite(kv_scale))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "q_scale and kv_scale must be finite");
+  if (pl.ws_bytes > 0) {
+    if (workspace == nullptr)
+      return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "workspace is NULL; %zu bytes needed", pl.ws_bytes);
+    if (d->workspace_bytes < pl.ws_bytes)
+      return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "workspace holds %llu bytes; %zu needed",
+                  (unsigned long long)d->workspace_bytes, pl.ws_bytes);
+    if (misaligned(workspace, 256))
+      return fail(PKV_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  }
+
+  pkv::Params p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.page_table = page_table;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.ws_o = pl.ws_bytes ? (float*)workspace : nullptr;
+  p.ws_ml = pl.ws_bytes ? (float2*)((char*)workspace + pl.ws_ml_off) : nullptr;
+  p.sinks = sinks;
+  p.mask = Tq > 1 ? mask : nullptr;
+  const int64_t Dk = d->head_dim_qk, Dv = d->head_dim_v;
+  const int64_t vrow = pl.path == PKV_PATH_MFMA_MLA ? Dk : Dv;
+  if (layout == PKV_NHD) {
+    p.k_page = (int64_t)ps * Hkv * Dk; p.k_slot = (int64_t)Hkv * Dk; p.k_head = Dk;
+    p.v_page = (int64_t)ps * Hkv * vrow; p.v_slot = (int64_t)Hkv * vrow; p.v_head = vrow;
+  } else {
+    p.k_page = (int64_t)Hkv * ps * Dk; p.k_slot = Dk; p.k_head = (int64_t)ps * Dk;
+    p.v_page = (int64_t)Hkv * ps * vrow; p.v_slot = vrow; p.v_head = (int64_t)ps * vrow;
+  }
+  p.B = d->batch;
+  p.Tq = Tq;
+  p.Hq = d->num_q_heads;
+  p.Hkv = Hkv;
+  p.G = d->num_q_heads / Hkv;
+  p.R = pl.rows;
+  p.Dqk = (int)Dk;
+  p.Dv = (int)Dv;
+  p.ps = ps;
+  p.pps = d->pages_per_seq;
+  p.num_pages = d->num_pages;
+  p.window = window;
+  p.mask_words16 = ((Tq + 31) / 32) * 2;
+  p.split_pages = pl.split_pages;
+  p.max_splits = pl.max_splits;
+  p.qk_scale_log2 = (float)((double)q_scale * (double)kv_scale / std::sqrt((double)Dk) *
+                            1.4426950408889634);
+  p.out_scale = kv_scale;
+  if (p.B > 65535 || Hkv > 65535)
+    return fail(PKV_ERR_UNSUPPORTED, "batch and num_kv_heads must be <= 65535");
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  switch (pl.path) {
+    case PKV_PATH_VALU: e = pkv::launch_split_valu(d->q_dtype, d->kv_dtype, (int)Dk, p, s); break;
+    case PKV_PATH_MFMA_MLA: e = pkv::launch_split_mla(d->q_dtype, p, s); break;
+    default: e = pkv::launch_split_mfma16(d->q_dtype, d->kv_dtype, (int)Dk, p, s); break;
+  }
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "split-KV launch failed: %s", hipGetErrorString(e));
+  if (opts && opts->split_event) {
+    e = hipEventRecord((hipEvent_t)opts->split_event, s);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "event record failed: %s", hipGetErrorString(e));
+  }
+  e = pkv::launch_combine(d->q_dtype, p, s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
+  g_err.clear();
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+pkv_status pkv_query_plan(const pkv_dims* dims, int num_kv_heads, int page_size, int window,
+                          int q_seq_len, const pkv_options* opts, pkv_plan_info* info) {
+  if (info == nullptr) return fail(PKV_ERR_INVALID_ARGUMENT, "info is NULL");
+  Plan pl;
+  // the latent shape is only reachable with an aliased cache; assume it
+  const bool aliased = dims != nullptr && dims->head_dim_v < dims->head_dim_qk;
+  pkv_status st = make_plan(dims, num_kv_heads, page_size, PKV_NHD, window, q_seq_len, aliased,
+                            opts, &pl);
+  if (st != PKV_OK) return st;
+  info->path = pl.path;
+  info->split_pages = pl.split_pages;
+  info->max_splits = pl.max_splits;
+  info->rows = pl.rows;
+  info->ctas_per_split_grid = pl.max_splits * num_kv_heads * dims->batch;
+  info->num_cus = pl.num_cus;
+  info->workspace_bytes = pl.ws_bytes;
+  g_err.clear();
+  return PKV_OK;
+}
+
+size_t pkv_workspace_size(const pkv_dims* dims, int num_kv_heads, int page_size, int window,
+                          int q_seq_len) {
+  Plan pl;
+  const bool aliased = dims != nullptr && dims->head_dim_v < dims->head_dim_qk;
+  if (make_plan(dims, num_kv_heads, page_size, PKV_NHD, window, q_seq_len, aliased, nullptr,
+                &pl) != PKV_OK)
+    return 0;
+  return pl.ws_bytes;
+}
+
+pkv_status pkv_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* page_table, const uint32_t* seq_lens, void* out,
+                           void* workspace, int num_kv_heads, int page_size, int layout,
+                           const float* sinks, float q_scale, float kv_scale, int window,
+                           int q_seq_len, const uint16_t* mask, void* stream,
+                           const pkv_dims* dims) {
+  return decode(q, k_cache, v_cache, page_table, seq_lens, out, workspace, num_kv_heads,
+                page_size, layout, sinks, q_scale, kv_scale, window, q_seq_len, mask, stream,
+                dims, nullptr);
+}
+
+pkv_status pkv_decode_attn_ex(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* page_table, const uint32_t* seq_lens, void* out,
+                              void* workspace, int num_kv_heads, int page_size, int layout,
+                              const float* sinks, float q_scale, float kv_scale, int window,
+                              int q_seq_len, const uint16_t* mask, void* stream,
+                              const pkv_dims* dims, const pkv_options* opts) {
+  return decode(q, k_cache, v_cache, page_table, seq_lens, out, workspace, num_kv_heads,
+                page_size, layout, sinks, q_scale, kv_scale, window, q_seq_len, mask, stream,
+                dims, opts);
+}
+
+pkv_status pkv_validate_inputs(const int32_t* page_table, const uint32_t* seq_lens,
+                               int num_kv_heads, int page_size, int window, int q_seq_len,
+                               void* stream, const pkv_dims* dims) {
+  Plan pl;
+  const bool aliased = dims != nullptr && dims->head_dim_v < dims->head_dim_qk;
+  pkv_options o{};
+  o.num_cus = 256;  // the plan is not used; avoid a device query
+  pkv_status st = make_plan(dims, num_kv_heads, page_size, PKV_NHD, window, q_seq_len, aliased,
+                            &o, &pl);
+  if (st != PKV_OK) return st;
+  if (dims->batch == 0) return PKV_OK;
+  if (!page_table || !seq_lens)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "page_table and seq_lens must not be NULL");
+  const int B = dims->batch, pps = dims->pages_per_seq;
+  std::vector<uint32_t> L(B);
+  std::vector<int32_t> T((size_t)B * pps);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(L.data(), seq_lens, sizeof(uint32_t) * B, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(T.data(), page_table, sizeof(int32_t) * T.size(), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "copying metadata failed: %s", hipGetErrorString(e));
+  const int64_t cap = (int64_t)pps * page_size;
+  for (int b = 0; b < B; ++b) {
+    const int64_t Lb = L[b];
+    if (Lb > cap)
+      return fail(PKV_ERR_DEVICE_DATA, "sequence %d: seq_len %lld exceeds pages_per_seq * "
+                                       "page_size = %lld", b, (long long)Lb, (long long)cap);
+    if (Lb < q_seq_len)
+      return fail(PKV_ERR_DEVICE_DATA, "sequence %d: seq_len %lld is shorter than q_seq_len %d",
+                  b, (long long)Lb, q_seq_len);
+    int64_t lo = 0;
+    if (window > 0) lo = std::max<int64_t>(0, Lb - q_seq_len + 1 - window);
+    for (int64_t pg = lo / page_size; pg < cdiv(Lb, page_size); ++pg) {
+      const int32_t id = T[(size_t)b * pps + pg];
+      if (id < 0 || id >= dims->num_pages)
+        return fail(PKV_ERR_DEVICE_DATA, "sequence %d: page_table[%d][%lld] = %d is outside "
+                                         "[0, %d)", b, b, (long long)pg, id, dims->num_pages);
+    }
+  }
+  g_err.clear();
+  return PKV_OK;
+}
+
+}  // extern "C"

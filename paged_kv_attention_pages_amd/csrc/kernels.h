@@ -1,0 +1,25 @@
+// kernels.h -- launchers of the decode kernels (host side of the HIP path).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "pkv_device.h"
+
+namespace pkv {
+
+// Split-KV decode on the matrix cores, up to 16 rows per KV head,
+// head_dim_qk == head_dim_v in {64, 128, 256}.
+hipError_t launch_split_mfma16(int q_dtype, int kv_dtype, int D, const Params& p, hipStream_t s);
+
+// Split-KV decode over a latent cache: one KV head, up to 64 rows, 576-wide
+// rows whose leading 512 entries are V.
+hipError_t launch_split_mla(int q_dtype, const Params& p, hipStream_t s);
+
+// Split-KV decode on the vector ALUs, up to 8 rows per KV head.
+hipError_t launch_split_valu(int q_dtype, int kv_dtype, int D, const Params& p, hipStream_t s);
+
+// Log-sum-exp merge of the split partials of every sequence that needed
+// more than one split (zeros for sequences with nothing visible).
+hipError_t launch_combine(int q_dtype, const Params& p, hipStream_t s);
+
+}  // namespace pkv

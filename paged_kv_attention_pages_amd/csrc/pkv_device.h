@@ -1,0 +1,205 @@
+// pkv_device.h -- device-side building blocks shared by the decode kernels.
+//
+// Kernel parameter block, sequence/split geometry, element conversions and
+// the matrix-core (MFMA) wrappers for gfx950.  Everything here is HIP-path
+// code; the CPU oracle shares none of it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// element codes (match pkv_dtype in include/pkv.h)
+enum : int { kF16 = 0, kBF16 = 1, kFP8 = 2 };
+
+// Parameters of one decode call, passed by value to every kernel.
+struct Params {
+  const void* q;              // [B, Tq, Hq, Dqk]
+  const void* k;              // paged K cache
+  const void* v;              // paged V cache (== k for the latent cache)
+  const int32_t* page_table;  // [B, pps]
+  const uint32_t* seq_lens;   // [B]
+  void* out;                  // [B, Tq, Hq, Dv]
+  float* ws_o;                // [B, Hkv, S, R, Dv] unnormalised partial outputs
+  float2* ws_ml;              // [B, Hkv, S, R] (running max in log2 units, sum)
+  const float* sinks;         // [Hkv, G] or null
+  const uint16_t* mask;       // [B, Tq, mask_words16] or null
+  int64_t k_page, k_slot, k_head;  // element strides of the K cache
+  int64_t v_page, v_slot, v_head;  // element strides of the V cache
+  int B, Tq, Hq, Hkv, G, R, Dqk, Dv;
+  int ps, pps, num_pages, window, mask_words16;
+  int split_pages, max_splits;
+  float qk_scale_log2;        // q_scale * kv_scale / sqrt(Dqk) * log2(e)
+  float out_scale;            // kv_scale (V dequantisation, applied once)
+};
+
+// Token range of sequence b that any of its query rows can see, and the
+// split-KV chunking of the pages that hold it.  Shared by the split and the
+// combine kernels so both agree on the number of splits of a sequence.
+struct SeqGeom {
+  int L;        // length, clamped to pps * ps
+  int lo;       // first token visible to the earliest query row
+  int p0;       // first page holding a visible token
+  int npages;   // pages from p0 through the one holding token L-1
+  int nsplits;  // ceil(npages / split_pages)
+};
+
+__device__ __forceinline__ SeqGeom seq_geom(const Params& p, int b) {
+  SeqGeom g;
+  uint32_t Lraw = p.seq_lens[b];
+  int cap = p.pps * p.ps;
+  g.L = Lraw > (uint32_t)cap ? cap : (int)Lraw;
+  int lo = 0;
+  if (p.window > 0) {
+    lo = g.L - p.Tq + 1 - p.window;
+    lo = lo < 0 ? 0 : lo;
+  }
+  g.lo = lo;
+  if (g.L <= lo) {
+    g.p0 = 0;
+    g.npages = 0;
+    g.nsplits = 0;
+    return g;
+  }
+  g.p0 = lo / p.ps;
+  g.npages = (g.L + p.ps - 1) / p.ps - g.p0;
+  g.nsplits = (g.npages + p.split_pages - 1) / p.split_pages;
+  return g;
+}
+
+// ---------------------------------------------------------------- vectors
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// D(16x16) += A(16x32) * B(32x16).  Lane l supplies A[l%16][8(l/16)..+8] and
+// B[8(l/16)..+8][l%16] as eight 16-bit values in four dwords; it receives
+// D[4(l/16)+i][l%16], i = 0..3.
+template <int QT>
+__device__ __forceinline__ f32x4 mfma_k32(uint4 a, uint4 b, f32x4 c) {
+  if constexpr (QT == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// D(16x16) += A(16x16) * B(16x16).  Lane l supplies A[l%16][4(l/16)..+4] and
+// B[4(l/16)..+4][l%16] as four 16-bit values in two dwords.
+template <int QT>
+__device__ __forceinline__ f32x4 mfma_k16(uint2 a, uint2 b, f32x4 c) {
+  if constexpr (QT == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a),
+                                                     __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------ conversions
+// Two fp32 -> packed 16-bit pair (round to nearest even), low half = x.
+template <int QT>
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  if constexpr (QT == kBF16) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f16x2 v = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// Four OCP e4m3fn bytes -> four fp32 (exact).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo[0];
+  f[1] = lo[1];
+  f[2] = hi[0];
+  f[3] = hi[1];
+}
+
+// Four e4m3fn bytes -> two dwords of the 16-bit compute type.  Every e4m3fn
+// value is exact in bf16 and in f16, so this conversion is exact.
+template <int QT>
+__device__ __forceinline__ uint2 fp8x4_to_16(uint32_t w) {
+  float f[4];
+  fp8x4_to_f32(w, f);
+  if constexpr (QT == kBF16) {
+    // exact in bf16: keep the upper half of each fp32
+    uint32_t a = (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+    uint32_t b = (__float_as_uint(f[2]) >> 16) | (__float_as_uint(f[3]) & 0xffff0000u);
+    return make_uint2(a, b);
+  } else {
+    return make_uint2(pack2<QT>(f[0], f[1]), pack2<QT>(f[2], f[3]));
+  }
+}
+
+// 16-bit element e (0..7) of a uint4, as the low 16 bits of a dword.
+__device__ __forceinline__ uint32_t half_of(const uint4& v, int e) {
+  uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// Butterfly max across the four 16-lane rows of a wave (lanes l, l^16,
+// l^32, l^48): every lane ends with the max of its column.
+__device__ __forceinline__ float max_across_rows(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float sum_across_rows(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Row r of the (G * Tq) rows sharing one KV head: query token r / G, head
+// kvh * G + r % G.
+__device__ __forceinline__ int64_t q_row_offset(const Params& p, int b, int kvh, int r) {
+  int iq = r / p.G, gh = r - iq * p.G;
+  return ((int64_t)(b * p.Tq + iq) * p.Hq + kvh * p.G + gh);
+}
+
+// Visibility of token t to query row r (the window and the spec-decode mask;
+// t < L is part of the test).  Written without branches or short-circuit
+// operators: the result feeds a select, and divergent early returns here
+// were structured wrongly by the compiler for the first element of the
+// score fragment (the bit test was dropped), so every term is evaluated and
+// combined with bitwise operators.
+struct RowVis {
+  int lo;          // first visible token (window), may be negative
+  int draft0;      // first draft position L - Tq (mask applies from here)
+  uint32_t bits;   // draft mask bits of this row (all ones without a mask)
+  __device__ __forceinline__ bool operator()(int t, int L) const {
+    const uint32_t sh = (uint32_t)(t - draft0) & 31u;
+    const bool in_range = (t >= lo) & (t < L);
+    const bool drafted = (t < draft0) | (((bits >> sh) & 1u) != 0u);
+    return in_range & drafted;
+  }
+};
+
+__device__ __forceinline__ RowVis row_vis(const Params& p, int b, int L, int r) {
+  RowVis v;
+  int iq = r / p.G;
+  v.lo = p.window > 0 ? L - p.Tq + iq - p.window + 1 : INT32_MIN;
+  if (p.Tq > 1 && p.mask != nullptr) {
+    v.draft0 = L - p.Tq;
+    const uint16_t* row = p.mask + ((int64_t)b * p.Tq + iq) * p.mask_words16;
+    v.bits = (uint32_t)row[0] | ((uint32_t)row[1] << 16);
+  } else {
+    v.draft0 = INT32_MAX;
+    v.bits = 0xffffffffu;
+  }
+  return v;
+}
+
+}  // namespace pkv

@@ -208,25 +208,25 @@ def make_inputs(w: Workload, seed: int, device="cpu", *, seq_lens=None, keep_fro
     if poison:
         nan = _nan_of(w.kv_dtype, dev)
         caches = [k_cache] if w.v_from_k else [k_cache, v_cache]
-        used = set(int(p) for p in perm[:total])
-        unused = [p for p in range(num_pages) if p not in used]
-        if unused:
-            idx = torch.tensor(unused, device=dev)
-            for c in caches:
-                c[idx] = nan
+        used = torch.zeros(num_pages, dtype=torch.bool)
+        used[perm[:total]] = True
+        whole = [int(x) for x in torch.nonzero(~used).flatten()]   # unused pages
+        partial = []                                               # (page, first, end) slots
         kf = None if keep_from is None else torch.as_tensor(keep_from, dtype=torch.int64)
         for b in range(B):
             Lb = int(L[b])
-            tail = Lb % ps
-            for c in caches:
-                if tail:
-                    _poison_slots(c, w.kv_layout, int(table[b, need[b] - 1]), tail, ps, nan)
-                if kf is not None and int(kf[b]) > 0:
-                    first = int(kf[b])
-                    for pg in range(first // ps):
-                        c[int(table[b, pg])] = nan
-                    if first % ps:
-                        _poison_slots(c, w.kv_layout, int(table[b, first // ps]), 0, first % ps, nan)
+            if Lb % ps:
+                partial.append((int(table[b, need[b] - 1]), Lb % ps, ps))
+            if kf is not None and int(kf[b]) > 0:
+                first = min(int(kf[b]), Lb)
+                whole.extend(int(x) for x in table[b, :first // ps])
+                if first % ps:
+                    partial.append((int(table[b, first // ps]), 0, first % ps))
+        for c in caches:
+            if whole:
+                c[torch.tensor(whole, device=dev)] = nan
+            for page, s0, s1 in partial:
+                _poison_slots(c, w.kv_layout, page, s0, s1, nan)
 
     return {
         "q": q, "k_cache": k_cache, "v_cache": v_cache,

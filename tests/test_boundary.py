@@ -1,0 +1,185 @@
+"""Host-side tests of the C-ABI library (no GPU needed).
+
+- libpkv.so loads and exports every function include/pkv.h declares;
+- the ctypes structs of the binding match the header's layout (a tiny C
+  program built with gcc prints sizeof/offsetof);
+- argument validation rejects what the xqa page rules out, with a message,
+  before anything is launched;
+- the split planner's choices (paths, split sizes, workspace sizes).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import paged_kv_attention_pages_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"pkv_decode_attn", "pkv_workspace_size", "pkv_last_error",
+            "pkv_validate_inputs"} <= set(names)
+    L = pkv.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", pkv.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (pkv_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+    assert pkv.lib().pkv_abi_version() == 1
+
+
+def test_struct_layouts_match_header(tmp_path):
+    prog = tmp_path / "layout.c"
+    prog.write_text("""
+#include <stddef.h>
+#include <stdio.h>
+#include "pkv.h"
+#define F(T, m) printf(#T "." #m " %zu\\n", offsetof(T, m));
+int main(void) {
+  printf("pkv_dims %zu\\n", sizeof(pkv_dims));
+  printf("pkv_options %zu\\n", sizeof(pkv_options));
+  printf("pkv_plan_info %zu\\n", sizeof(pkv_plan_info));
+  F(pkv_dims, workspace_bytes) F(pkv_dims, kv_dtype) F(pkv_options, target_ctas) F(pkv_options, split_event)
+  F(pkv_plan_info, workspace_bytes) F(pkv_plan_info, num_cus)
+  return 0;
+}
+""")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), str(prog), "-o", str(exe)],
+                   check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    assert int(got["pkv_dims"]) == ctypes.sizeof(pkv.Dims)
+    assert int(got["pkv_options"]) == ctypes.sizeof(pkv.Options)
+    assert int(got["pkv_plan_info"]) == ctypes.sizeof(pkv.PlanInfo)
+    assert int(got["pkv_dims.workspace_bytes"]) == pkv.Dims.workspace_bytes.offset
+    assert int(got["pkv_dims.kv_dtype"]) == pkv.Dims.kv_dtype.offset
+    assert int(got["pkv_options.target_ctas"]) == pkv.Options.target_ctas.offset
+    assert int(got["pkv_options.split_event"]) == pkv.Options.split_event.offset
+    assert int(got["pkv_plan_info.workspace_bytes"]) == pkv.PlanInfo.workspace_bytes.offset
+    assert int(got["pkv_plan_info.num_cus"]) == pkv.PlanInfo.num_cus.offset
+
+
+BASE = dict(batch=64, num_q_heads=32, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
+            pages_per_seq=128, page_size=64, q_dtype=torch.bfloat16, num_cus=256)
+
+
+def plan(**kw):
+    a = dict(BASE)
+    a.update(kw)
+    return pkv.query_plan(**a)
+
+
+def test_plan_paths():
+    assert plan()["path"] == pkv.PATH_MFMA
+    assert plan(path="valu")["path"] == pkv.PATH_VALU
+    mla = plan(batch=32, num_q_heads=64, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
+               pages_per_seq=256)
+    assert mla["path"] == pkv.PATH_MFMA_MLA and mla["rows"] == 64
+    spec = plan(q_seq_len=4)
+    assert spec["rows"] == 16 and spec["path"] == pkv.PATH_MFMA
+    fp8 = plan(batch=128, num_q_heads=64, kv_dtype=torch.float8_e4m3fn, page_size=32,
+               pages_per_seq=1024, window=4096)
+    assert fp8["rows"] == 8
+
+
+def test_plan_window_bounds_splits():
+    # a 4096-token window over 32-token pages touches at most 129 pages
+    p = plan(batch=128, num_q_heads=64, kv_dtype=torch.float8_e4m3fn, page_size=32,
+             pages_per_seq=1024, window=4096)
+    assert p["split_pages"] * p["max_splits"] >= 129
+    assert (p["max_splits"] - 1) * p["split_pages"] < 129
+
+
+def test_plan_forced_split_and_workspace():
+    p = plan(split_pages=1)
+    assert p["split_pages"] == 1 and p["max_splits"] == 128
+    rows = 4
+    want_o = 64 * 8 * 128 * rows * 128 * 4
+    assert p["workspace_bytes"] >= want_o + 64 * 8 * 128 * rows * 8
+    one = plan(split_pages=128)
+    assert one["max_splits"] == 1 and one["workspace_bytes"] == 0
+    assert pkv.workspace_size(**{k: v for k, v in BASE.items() if k != "num_cus"}) > 0
+
+
+def test_plan_split_sizes_multiple_of_pages_and_at_least_256_tokens():
+    for ps in (16, 32, 64, 128):
+        p = plan(page_size=ps, pages_per_seq=8192 // ps)
+        assert p["split_pages"] * ps >= 256
+        assert p["split_pages"] * p["max_splits"] >= 8192 // ps
+
+
+@pytest.mark.parametrize("kw, status, msg", [
+    (dict(page_size=48), 1, "page_size"),
+    (dict(num_kv_heads=5), 1, "multiple of num_kv_heads"),
+    (dict(window=-1), 1, "window"),
+    (dict(q_seq_len=0), 1, "q_seq_len"),
+    (dict(head_dim_qk=96, head_dim_v=96), 2, "unsupported shape"),
+    (dict(head_dim_qk=576, head_dim_v=512, num_kv_heads=1, num_q_heads=64, kv_dtype=torch.float8_e4m3fn), 2, ""),
+    (dict(q_seq_len=5), 2, "rows"),
+    (dict(path="valu", q_seq_len=4), 2, "vector path"),
+    (dict(path="mfma_mla"), 2, "latent path"),
+    (dict(kv_dtype=torch.float16), 1, "KV cache dtype"),
+    (dict(pages_per_seq=0), 1, "pages_per_seq"),
+])
+def test_plan_rejects(kw, status, msg):
+    with pytest.raises(pkv.PkvError) as e:
+        plan(**kw)
+    assert e.value.status == status
+    assert msg in str(e.value)
+
+
+def _raw_decode(**over):
+    """Call pkv_decode_attn directly with fake pointers; validation must fail first."""
+    d = pkv.Dims(64, 32, 128, 128, 128, 1000, 1, 1, 1 << 30)
+    args = dict(q=8192, k=8192, v=8192, pt=8192, sl=8192, out=8192, ws=8192, hkv=8, ps=64,
+                layout=0, sinks=None, qs=1.0, ks=1.0, win=0, tq=1, mask=None, stream=None, dims=d)
+    args.update(over)
+    L = pkv.lib()
+    st = L.pkv_decode_attn(*[ctypes.c_void_p(a) if isinstance(a, int) else a for a in (
+        args["q"], args["k"], args["v"], args["pt"], args["sl"], args["out"], args["ws"])],
+        args["hkv"], args["ps"], args["layout"], args["sinks"], args["qs"], args["ks"],
+        args["win"], args["tq"], args["mask"], args["stream"], ctypes.byref(args["dims"]))
+    return st, L.pkv_last_error().decode()
+
+
+def test_decode_rejects_before_launch():
+    assert _raw_decode(ps=12)[0] == 1
+    assert _raw_decode(layout=7)[0] == 1
+    st, msg = _raw_decode(q=None)
+    assert st == 1 and "NULL" in msg
+    st, msg = _raw_decode(q=8200)
+    assert st == 1 and "aligned" in msg
+    st, msg = _raw_decode(dims=pkv.Dims(64, 32, 128, 128, 128, 1000, 1, 1, 16))
+    assert st == 3 and "workspace" in msg
+    st, msg = _raw_decode(qs=float("nan"))
+    assert st == 1 and "finite" in msg
+    st, msg = _raw_decode(dims=pkv.Dims(64, 32, 128, 128, 128, 1000, 0, 1, 1 << 30))
+    assert st == 1 and "KV cache dtype" in msg
+
+
+def test_zero_batch_is_a_noop():
+    st, msg = _raw_decode(dims=pkv.Dims(0, 32, 128, 128, 128, 1000, 1, 1, 0), q=None, out=None)
+    assert st == 0, msg
+
+
+def test_binding_rejects_cpu_tensors():
+    q = torch.zeros(2, 1, 4, 128, dtype=torch.float16)
+    k = torch.zeros(4, 16, 1, 128, dtype=torch.float16)
+    with pytest.raises(pkv.PkvError, match="GPU"):
+        pkv.decode_attn(q, k, k, torch.zeros(2, 4, dtype=torch.int32),
+                        torch.zeros(2, dtype=torch.int32), torch.empty_like(q),
+                        num_kv_heads=1, page_size=16)

@@ -1,0 +1,365 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (max-abs on N(0,1) inputs): 4e-3 for fp16, 1e-2 for bf16, 2e-2
+for an fp8 cache (the oracle reads the same e4m3fn bytes and kv_scale).
+Index work is checked exactly: single-token sequences must return their V
+row bit for bit, page permutation and NHD/HND must not change a single bit,
+NaN poison in every unused page and invisible slot must never reach the
+output, and every output element must be written (outputs start as NaN).
+"""
+import math
+
+import pytest
+import torch
+
+import oracle
+import paged_kv_attention_pages_amd as pkv
+from paged_kv_attention_pages_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def tol_for(w):
+    if w.kv_dtype == torch.float8_e4m3fn:
+        return 2e-2
+    return 4e-3 if w.q_dtype == torch.float16 else 1e-2
+
+
+def keep_from(w, L):
+    """Start of the range any query row can see (the window reading)."""
+    if w.window <= 0:
+        return None
+    return (L - w.q_seq_len + 1 - w.window).clamp(min=0)
+
+
+def make(w, seed, seq_lens=None):
+    L = synth.draw_seq_lens(w, seed) if seq_lens is None else torch.as_tensor(seq_lens)
+    return synth.make_inputs(w, seed, DEV, seq_lens=L, keep_from=keep_from(w, L))
+
+
+def run_gpu(w, inp, **kw):
+    B = inp["q"].shape[0]
+    out = torch.full((B, w.q_seq_len, w.num_q_heads, w.head_dim_v), float("nan"),
+                     dtype=w.q_dtype, device=DEV)
+    pkv.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"], inp["seq_lens"],
+                    out, num_kv_heads=w.num_kv_heads, page_size=w.page_size, sinks=inp["sinks"],
+                    q_scale=w.q_scale, kv_scale=w.kv_scale, sliding_win_size=w.window,
+                    kv_layout=w.kv_layout, q_seq_len=w.q_seq_len, mask=inp["mask"],
+                    head_dim_v=w.head_dim_v, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _take(t, idx):
+    """Rows idx of a small per-sequence tensor, on the host (uint16 has no index kernel)."""
+    if t is None:
+        return None
+    t = t.cpu()
+    if t.dtype == torch.uint16:
+        return t.view(torch.int16)[idx].view(torch.uint16)
+    return t[idx]
+
+
+def run_oracle(w, inp, idx=None):
+    sel = (lambda t: t) if idx is None else (lambda t: _take(t, idx))
+    return oracle.decode(sel(inp["q"]), inp["k_cache"], None if w.v_from_k else inp["v_cache"],
+                         sel(inp["page_table"]), sel(inp["seq_lens"]), sinks=inp["sinks"],
+                         mask=sel(inp["mask"]), head_dim_v=w.head_dim_v, v_from_k=w.v_from_k,
+                         **synth.decode_kwargs(w))
+
+
+def assert_parity(w, got, ref, label=""):
+    got = got.double().cpu()
+    assert not torch.isnan(got).any(), f"{label}: NaN in output (unwritten or poisoned)"
+    err = (got - ref).abs().max().item()
+    rms = ref.pow(2).mean().sqrt().item()
+    print(f"[parity] {label} max_abs={err:.3e} tol={tol_for(w):.0e} rms_ref={rms:.3e}", flush=True)
+    assert err <= tol_for(w), f"{label}: max abs err {err} > {tol_for(w)}"
+
+
+# ---------------------------------------------------------------- small cases
+
+SMALL = {
+    "tiny": synth.WORKLOADS["tiny"],
+    "gqa": synth.WORKLOADS["llama3_8b_gqa"].replace(batch=6, seq_len_range=(1, 1500)),
+    "fp8": synth.WORKLOADS["fp8_window_sinks"].replace(
+        batch=5, num_q_heads=16, num_kv_heads=2, seq_len_range=(100, 1200), window=300),
+    "spec": synth.WORKLOADS["spec_decode"].replace(batch=5, seq_len_range=(4, 1200)),
+    "mla": synth.WORKLOADS["mla"].replace(batch=3, seq_len_range=(1, 900)),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("split", [0, 1, 1000])
+def test_small_parity(name, split):
+    w = SMALL[name]
+    print(f"[case] small {name} split_pages={split}", flush=True)
+    inp = make(w, seed=31)
+    got = run_gpu(w, inp, split_pages=split)
+    assert_parity(w, got, run_oracle(w, inp), f"{name}/split{split}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "gqa", "fp8"])
+@pytest.mark.parametrize("split", [0, 1])
+def test_valu_path_parity(name, split):
+    w = SMALL[name]
+    print(f"[case] valu {name} split_pages={split}", flush=True)
+    inp = make(w, seed=32)
+    got = run_gpu(w, inp, path="valu", split_pages=split)
+    assert_parity(w, got, run_oracle(w, inp), f"valu/{name}/split{split}")
+
+
+@pytest.mark.parametrize("ps", [16, 32, 64, 128])
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+@pytest.mark.parametrize("path", ["mfma", "valu"])
+def test_page_sizes_and_layouts(ps, layout, path):
+    w = SMALL["gqa"].replace(page_size=ps, kv_layout=layout, seq_len_range=(1, 700), batch=4)
+    print(f"[case] ps={ps} {layout} {path}", flush=True)
+    inp = make(w, seed=33 + ps)
+    got = run_gpu(w, inp, path=path, split_pages=2)
+    assert_parity(w, got, run_oracle(w, inp), f"ps{ps}/{layout}/{path}")
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_other_head_dims(D):
+    w = SMALL["gqa"].replace(head_dim_qk=D, head_dim_v=D, batch=3, seq_len_range=(1, 600))
+    print(f"[case] head_dim {D}", flush=True)
+    inp = make(w, seed=40 + D)
+    got = run_gpu(w, inp, split_pages=3)
+    assert_parity(w, got, run_oracle(w, inp), f"D{D}")
+
+
+def test_fp16_query_fp8_cache():
+    w = SMALL["fp8"].replace(q_dtype=torch.float16)
+    print("[case] f16 q + fp8 cache", flush=True)
+    inp = make(w, seed=41)
+    for path in ("mfma", "valu"):
+        got = run_gpu(w, inp, path=path, split_pages=2)
+        assert_parity(w, got, run_oracle(w, inp), f"f16q-fp8/{path}")
+
+
+@pytest.mark.parametrize("kind", ["causal", "random", "ones"])
+@pytest.mark.parametrize("W", [0, 50])
+def test_spec_decode_masks(kind, W):
+    w = SMALL["spec"].replace(mask=kind, window=W)
+    print(f"[case] spec mask={kind} window={W}", flush=True)
+    inp = make(w, seed=42)
+    got = run_gpu(w, inp, split_pages=1)
+    assert_parity(w, got, run_oracle(w, inp), f"spec/{kind}/W{W}")
+
+
+def test_spec_16_rows_one_kv_head_per_query_head():
+    # q_seq_len 16 with group 1: a full 16-row tile of query tokens
+    w = SMALL["spec"].replace(num_q_heads=4, num_kv_heads=4, q_seq_len=16, mask="random",
+                              seq_len_range=(16, 700))
+    print("[case] spec Tq=16 G=1", flush=True)
+    inp = make(w, seed=43)
+    got = run_gpu(w, inp, split_pages=2)
+    assert_parity(w, got, run_oracle(w, inp), "spec/Tq16")
+
+
+def test_window_sinks_multi_split():
+    w = SMALL["fp8"].replace(window=700, seq_len_range=(1, 2500), batch=6)
+    print("[case] fp8 window 700 sinks, 1-page splits", flush=True)
+    inp = make(w, seed=44)
+    got = run_gpu(w, inp, split_pages=1)
+    assert_parity(w, got, run_oracle(w, inp), "fp8/W700")
+
+
+# ---------------------------------------------------------------- exact checks
+
+@pytest.mark.parametrize("name", ["tiny", "gqa", "mla"])
+def test_single_token_returns_v_row_exactly(name):
+    w = SMALL[name].replace(sinks=False, window=0)
+    B = 3
+    inp = make(w.replace(batch=B, fixed_seq_lens=(1,) * B, seq_len_range=None, num_pages=None),
+               seed=45)
+    got = run_gpu(w, inp)
+    t0 = inp["page_table_host"][:, 0].to(torch.int64)
+    src = inp["k_cache"] if w.v_from_k else inp["v_cache"]
+    for b in range(B):
+        for h in range(w.num_q_heads):
+            kvh = h // w.group
+            row = src[t0[b], 0, kvh] if w.kv_layout == "NHD" else src[t0[b], kvh, 0]
+            assert torch.equal(got[b, 0, h], row[: w.head_dim_v].to(w.q_dtype)), (b, h)
+
+
+@pytest.mark.parametrize("path", ["mfma", "valu"])
+def test_fp8_every_code_decodes_exactly(path):
+    # one-token sequences whose V rows hold all 256 e4m3fn codes: out must be
+    # exactly the decoded value (e4m3fn is a subset of bf16), NaN for NaN codes
+    w = SMALL["fp8"].replace(sinks=False, window=0, num_q_heads=2, num_kv_heads=1, kv_scale=1.0)
+    B = 2
+    inp = make(w.replace(batch=B, fixed_seq_lens=(1,) * B, seq_len_range=None), seed=46)
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(2, 128)
+    v = inp["v_cache"].view(torch.uint8)
+    k = inp["k_cache"].view(torch.uint8)
+    for b in range(B):
+        pg = int(inp["page_table_host"][b, 0])
+        v[pg, 0, 0] = codes[b].to(DEV)
+        k[pg, 0, 0] = 0x38  # 1.0, finite scores
+    torch.cuda.synchronize()
+    got = run_gpu(w, inp, path=path).float().cpu()
+    want = codes.view(torch.float8_e4m3fn).float()
+    for b in range(B):
+        for h in range(2):
+            g, r = got[b, 0, h], want[b]
+            assert torch.equal(torch.isnan(g), torch.isnan(r))
+            ok = ~torch.isnan(r)
+            assert torch.equal(g[ok], r[ok]), (b, h)
+    # cross-check the oracle's decoder on the same codes
+    for c in range(256):
+        o = oracle.decode_e4m3fn(c)
+        r = float(want.flatten()[c])
+        assert (math.isnan(o) and math.isnan(r)) or o == r
+
+
+def test_empty_and_ragged_sequences():
+    w = SMALL["gqa"].replace(batch=8)
+    lens = [0, 1, 15, 16, 17, 63, 65, 1023]
+    inp = make(w, seed=47, seq_lens=lens)
+    for split in (0, 1):
+        got = run_gpu(w, inp, split_pages=split)
+        assert torch.equal(got[0].float().cpu(), torch.zeros_like(got[0].float().cpu()))
+        assert_parity(w, got, run_oracle(w, inp), f"ragged/split{split}")
+
+
+def test_window_one_and_window_ge_len():
+    w = SMALL["gqa"].replace(batch=4, seq_len_range=(1, 500))
+    inp = make(w, seed=48)
+    base = run_gpu(w, inp)
+    wide = run_gpu(w.replace(window=10_000), inp)
+    assert torch.equal(base, wide)
+    one = run_gpu(w.replace(window=1), inp)
+    torch.testing.assert_close(one.double().cpu(), run_oracle(w.replace(window=1), inp),
+                               rtol=0, atol=1e-2)
+
+
+def test_no_visible_draft_row_gives_zeros():
+    # seq_len == q_seq_len and an all-zero mask row: query 0 sees nothing
+    w = SMALL["spec"].replace(batch=2, fixed_seq_lens=(4, 4), seq_len_range=None, mask="causal")
+    inp = make(w, seed=49)
+    inp["mask"].view(torch.int16)[:, 0] = 0
+    got = run_gpu(w, inp)
+    assert torch.equal(got[:, 0].float().cpu(), torch.zeros_like(got[:, 0].float().cpu()))
+    assert_parity(w, got, run_oracle(w, inp), "zero-row")
+
+
+def test_page_permutation_is_bit_identical():
+    w = SMALL["gqa"]
+    inp = make(w, seed=50)
+    base = run_gpu(w, inp, split_pages=2)
+    P = inp["num_pages"]
+    perm = torch.randperm(P, generator=torch.Generator().manual_seed(5))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(P)
+    inp2 = dict(inp)
+    perm_d = perm.to(DEV)
+    inp2["k_cache"] = inp["k_cache"][perm_d].contiguous()
+    inp2["v_cache"] = inp["v_cache"][perm_d].contiguous()
+    inp2["page_table"] = inv.to(DEV)[inp["page_table"].long()].to(torch.int32)
+    assert torch.equal(run_gpu(w, inp2, split_pages=2), base)
+
+
+def test_nhd_and_hnd_are_bit_identical():
+    w = SMALL["gqa"].replace(kv_layout="NHD")
+    inp = make(w, seed=51)
+    a = run_gpu(w, inp, split_pages=2)
+    inp2 = dict(inp)
+    inp2["k_cache"] = inp["k_cache"].transpose(1, 2).contiguous()
+    inp2["v_cache"] = inp["v_cache"].transpose(1, 2).contiguous()
+    b = run_gpu(w.replace(kv_layout="HND"), inp2, split_pages=2)
+    assert torch.equal(a, b)
+
+
+def test_validate_inputs_reports_bad_page_ids():
+    w = SMALL["gqa"]
+    inp = make(w, seed=52)
+    kw = dict(num_kv_heads=w.num_kv_heads, page_size=w.page_size)
+    pkv.validate_inputs(inp["q"], inp["k_cache"], inp["page_table"], inp["seq_lens"], **kw)
+    bad = inp["page_table"].clone()
+    bad[2, 0] = inp["num_pages"] + 5
+    with pytest.raises(pkv.PkvError, match="sequence 2"):
+        pkv.validate_inputs(inp["q"], inp["k_cache"], bad, inp["seq_lens"], **kw)
+
+
+def test_bad_arguments_raise():
+    w = SMALL["gqa"]
+    inp = make(w, seed=53)
+    with pytest.raises(pkv.PkvError, match="page_size"):
+        run_gpu(w.replace(page_size=48), inp)
+
+
+# ---------------------------------------------------------------- full sizes
+
+def _sample(L, k=6):
+    order = torch.argsort(L)
+    pick = [int(order[0]), int(order[-1])] + [int(i) for i in order[torch.linspace(
+        1, len(L) - 2, k - 2).long()]]
+    return torch.tensor(sorted(set(pick)))
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_full_size_sampled_parity(name):
+    w = synth.WORKLOADS[name]
+    print(f"[case] full {name}", flush=True)
+    inp = make(w, seed=1)
+    got = run_gpu(w, inp)
+    L = inp["seq_lens_host"]
+    idx = torch.arange(len(L)) if len(L) <= 8 else _sample(L, 6 if name != "mla" else 4)
+    ref = run_oracle(w, inp, idx)
+    assert_parity(w, got[idx.to(DEV)], ref, f"full/{name}")
+    assert not torch.isnan(got).any()
+
+
+# ---------------------------------------------------------------- exact visible sets
+
+def _probe(w, inp):
+    """q = 0 and V[t] = onehot(t): out[b, i, h, d] = 1/|visible| if token d is visible."""
+    inp["q"].zero_()
+    src = inp["k_cache"] if w.v_from_k else inp["v_cache"]
+    # write raw bits: 1.0 is 0x38 (e4m3fn), 0x3F80 (bf16), 0x3C00 (f16)
+    if src.dtype == torch.float8_e4m3fn:
+        src, one = src.view(torch.uint8), 0x38
+    else:
+        src, one = src.view(torch.int16), (0x3F80 if src.dtype == torch.bfloat16 else 0x3C00)
+    src.zero_()
+    for b in range(inp["q"].shape[0]):
+        L = int(inp["seq_lens_host"][b])
+        for t in range(L):
+            pg, sl = int(inp["page_table_host"][b, t // w.page_size]), t % w.page_size
+            if w.kv_layout == "NHD":
+                src[pg, sl, :, t] = one
+            else:
+                src[pg, :, sl, t] = one
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("case", [
+    ("spec", "causal", "mfma", 0), ("spec", "random", "mfma", 0), ("spec", "zero", "mfma", 0),
+    ("spec", "random", "mfma", 9), ("spec2", "causal", "valu", 0), ("spec2", "random", "valu", 7),
+    ("gqa", None, "mfma", 5), ("gqa", None, "valu", 5), ("fp8", None, "mfma", 11),
+    ("fp8", None, "valu", 11), ("mla", None, "mfma_mla", 0), ("mla4", "random", "mfma_mla", 0),
+])
+def test_visible_sets_exact(case):
+    name, mask, path, W = case
+    base = {
+        "spec": SMALL["spec"].replace(num_q_heads=8, num_kv_heads=2),
+        "spec2": SMALL["spec"].replace(num_q_heads=4, num_kv_heads=2),
+        "gqa": SMALL["gqa"], "fp8": SMALL["fp8"].replace(kv_scale=1.0, sinks=False),
+        "mla": SMALL["mla"], "mla4": SMALL["mla"].replace(num_q_heads=16, q_seq_len=4),
+    }[name]
+    w = base.replace(batch=3, fixed_seq_lens=(20, 37, 100), seq_len_range=None, page_size=16,
+                     window=W, mask=("causal" if mask == "zero" else mask) if base.q_seq_len > 1 or name == "mla4" else None)
+    print(f"[case] visible-set {case}", flush=True)
+    inp = make(w, seed=60)
+    if mask == "zero":
+        inp["mask"].view(torch.int16).zero_()
+    _probe(w, inp)
+    got = run_gpu(w, inp, path=path, split_pages=1).float().cpu()
+    ref = run_oracle(w, inp)
+    vis_got = got > 0
+    vis_ref = ref > 0
+    assert torch.equal(vis_got, vis_ref), f"visible sets differ at {torch.nonzero(vis_got != vis_ref)[:8].tolist()}"
+    torch.testing.assert_close(got.double(), ref, rtol=2 ** -7, atol=0)
