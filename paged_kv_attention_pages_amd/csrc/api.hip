@@ -147,12 +147,17 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
   // keep each split's partial-result traffic under ~1/8 of its cache bytes,
   // and every split at least 256 tokens long
   int64_t min_pages = std::max<int64_t>(cdiv(8 * partial_bytes, page_bytes), cdiv(256, ps));
-  const int64_t target = (opts && opts->target_ctas > 0) ? opts->target_ctas : 16LL * cus;
+  // the matrix-core path runs one wave per split and keeps a split's page ids
+  // one per lane (at most 64 pages); the others run four waves per split
+  const int64_t waves_per_cta = path == PKV_PATH_MFMA ? 1 : 4;
+  const int64_t max_sp = path == PKV_PATH_MFMA ? 64 : INT32_MAX;
+  const int64_t target =
+      (opts && opts->target_ctas > 0) ? opts->target_ctas : 32LL * cus / waves_per_cta / 4;
   int64_t sp = units > 0 ? cdiv(units * pages_max, target) : pages_max;
   sp = std::max(sp, min_pages);
   sp = std::min(sp, pages_max);
   if (opts && opts->split_pages > 0) sp = std::min<int64_t>(opts->split_pages, pages_max);
-  sp = std::max<int64_t>(sp, 1);
+  sp = std::max<int64_t>(std::min(sp, max_sp), 1);
   const int64_t S = cdiv(pages_max, sp);
   if (S > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many splits (%lld)", (long long)S);
 

@@ -100,6 +100,37 @@ __device__ __forceinline__ f32x4 mfma_k16(uint2 a, uint2 b, f32x4 c) {
                                                  __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
+// ------------------------------------------------------------ buffer loads
+// Raw buffer loads through a resource that spans one cache page: offsets are
+// 32-bit and relative to the page, and a resource with zero size makes every
+// load return zeros without touching memory -- used for pipeline slots past
+// the end of a split and for page ids outside the cache, so that every
+// pipeline step issues the same number of loads.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// N 32-bit words at byte offset voff + soff
+template <int N>
+__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint32_t* w) {
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 4 * i, soff, 0);
+      w[i] = a[0]; w[i + 1] = a[1]; w[i + 2] = a[2]; w[i + 3] = a[3];
+    }
+  } else if constexpr (N == 2) {
+    u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    w[0] = a[0]; w[1] = a[1];
+  } else {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  }
+}
+
 // ------------------------------------------------------------ conversions
 // Two fp32 -> packed 16-bit pair (round to nearest even), low half = x.
 template <int QT>

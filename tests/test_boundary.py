@@ -110,7 +110,8 @@ def test_plan_forced_split_and_workspace():
     rows = 4
     want_o = 64 * 8 * 128 * rows * 128 * 4
     assert p["workspace_bytes"] >= want_o + 64 * 8 * 128 * rows * 8
-    one = plan(split_pages=128)
+    assert plan(split_pages=128)["split_pages"] == 64   # one page id per lane
+    one = plan(split_pages=128, path="valu")
     assert one["max_splits"] == 1 and one["workspace_bytes"] == 0
     assert pkv.workspace_size(**{k: v for k, v in BASE.items() if k != "num_cus"}) > 0
 
