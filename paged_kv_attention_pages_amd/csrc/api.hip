@@ -58,6 +58,7 @@ struct Plan {
   int split_pages;
   int max_splits;
   int num_cus;
+  int sk_waves;        // > 0: stream-K over this many persistent waves
   size_t ws_o_bytes;   // partial outputs
   size_t ws_ml_off;    // offset of (max, sum) pairs
   size_t ws_bytes;
@@ -166,6 +167,21 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
   pl->split_pages = (int)sp;
   pl->max_splits = (int)S;
   pl->num_cus = cus;
+  pl->sk_waves = 0;
+  // Stream-K schedule (matrix-core path, batch <= 256, no forced split size):
+  // four persistent waves per CU (measured best: one per SIMD, each with a
+  // three-stage pipeline in flight); 2 partial slots per wave.
+  if (path == PKV_PATH_MFMA && d->batch <= 256 && !(opts && opts->split_pages > 0)) {
+    const int64_t W = (opts && opts->target_ctas > 0) ? opts->target_ctas : 4LL * cus;
+    pl->sk_waves = (int)std::min<int64_t>(W, 1 << 20);
+    pl->split_pages = 0;
+    pl->max_splits = 0;
+    const size_t nrow = (size_t)2 * pl->sk_waves * R;
+    pl->ws_o_bytes = nrow * Dv * sizeof(float);
+    pl->ws_ml_off = (pl->ws_o_bytes + 255) & ~(size_t)255;
+    pl->ws_bytes = pl->ws_ml_off + nrow * 2 * sizeof(float);
+    return PKV_OK;
+  }
   const size_t nrow = (size_t)d->batch * Hkv * S * R;
   if (S > 1) {
     pl->ws_o_bytes = nrow * Dv * sizeof(float);
@@ -241,6 +257,7 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
   p.mask_words16 = ((Tq + 31) / 32) * 2;
   p.split_pages = pl.split_pages;
   p.max_splits = pl.max_splits;
+  p.sk_waves = pl.sk_waves;
   p.qk_scale_log2 = (float)((double)q_scale * (double)kv_scale / std::sqrt((double)Dk) *
                             1.4426950408889634);
   p.out_scale = kv_scale;
@@ -286,7 +303,8 @@ pkv_status pkv_query_plan(const pkv_dims* dims, int num_kv_heads, int page_size,
   info->split_pages = pl.split_pages;
   info->max_splits = pl.max_splits;
   info->rows = pl.rows;
-  info->ctas_per_split_grid = pl.max_splits * num_kv_heads * dims->batch;
+  info->ctas_per_split_grid =
+      pl.sk_waves > 0 ? pl.sk_waves : pl.max_splits * num_kv_heads * dims->batch;
   info->num_cus = pl.num_cus;
   info->workspace_bytes = pl.ws_bytes;
   g_err.clear();

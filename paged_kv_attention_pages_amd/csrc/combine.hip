@@ -57,12 +57,102 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
   }
 }
 
+// Stream-K schedule: unit (b, kvh) was cut across waves w0..w1 when its tiles
+// span more than one wave's share.  Wave w0 left its piece in slot 2 w0 (when
+// the unit is its first) or 2 w0 + 1 (its last); every later wave up to w1
+// has the unit first and left slot 2 w.  Units held by one wave were finished
+// by the split kernel; units with no tiles get zeros here.
+// Grid (Hkv, B, row groups of 4); wave v merges row 4 * group + v.  Lane j
+// reads the (m, l) of slot j (in groups of 64), so the max and the
+// denominator are wave reductions; the slot weights are then broadcast with
+// readlane and eight slots' partial outputs are loaded at a time.
+template <int QT>
+__global__ __launch_bounds__(256) void combine_sk_kernel(Params p) {
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.z * 4 + (threadIdx.x >> 6);
+  if (r >= p.R) return;
+  const SkSched S = sk_schedule(p);
+  const int W = sk_waves_eff(S.T, p.sk_waves);
+  int pre, n;
+  sk_seq_of(S, b, &pre, &n);
+  uint16_t* o = (uint16_t*)p.out + q_row_offset(p, b, kvh, r) * p.Dv;
+  if (n == 0) {
+    for (int d = lane; d < p.Dv; d += 64) o[d] = 0;
+    return;
+  }
+  const int64_t us = (int64_t)pre * p.Hkv + (int64_t)kvh * n, ue = us + n;
+  const int w0 = sk_wave_of(S.T, us, W), w1 = sk_wave_of(S.T, ue - 1, W);
+  if (w0 == w1) return;
+  const int64_t slot0 = sk_wave_start(S.T, w0, W) == us ? 2 * (int64_t)w0 : 2 * (int64_t)w0 + 1;
+  const int nslots = w1 - w0 + 1;
+  auto row_of = [&](int j) -> int64_t {
+    return (j == 0 ? slot0 : 2 * (int64_t)(w0 + j)) * p.R + r;
+  };
+  float sk = kNegInf;
+  if (p.sinks != nullptr) sk = p.sinks[kvh * p.G + r % p.G] * kLog2e;
+  float M = sk;
+  for (int j0 = 0; j0 < nslots; j0 += 64) {
+    const int j = j0 + lane;
+    M = fmaxf(M, j < nslots ? p.ws_ml[row_of(j)].x : kNegInf);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
+  float den = p.sinks != nullptr ? exp2f(sk - M) : 0.f;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  const int per_lane = p.Dv >> 6;  // Dv in {64, 128, 256, 512}
+  for (int j0 = 0; j0 < nslots; j0 += 64) {
+    const int j = j0 + lane;
+    float wt = 0.f, lsum = 0.f;
+    if (j < nslots) {
+      const float2 ml = p.ws_ml[row_of(j)];
+      wt = ml.x == kNegInf ? 0.f : exp2f(ml.x - M);
+      lsum = wt * ml.y;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) lsum += __shfl_xor(lsum, d);
+    den += lsum;
+    const int cnt = min(64, nslots - j0);
+    for (int jb = 0; jb < cnt; jb += 8) {
+      float v[8][8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool ok = jb + u < cnt;
+        const float* src = p.ws_o + row_of(j0 + (ok ? jb + u : 0)) * p.Dv + lane;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[u][k] = (ok && k < per_lane) ? src[64 * k] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        // lanes past the last slot hold weight 0 (and their loads are zeros)
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), jb + u));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] += wj * v[u][k];
+      }
+    }
+  }
+  const float inv = den > 0.f ? p.out_scale / den : 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    if (k < per_lane) o[lane + 64 * k] = (uint16_t)(pack2<QT>(acc[k] * inv, 0.f) & 0xffffu);
+}
+
 hipError_t launch_combine(int q_dtype, const Params& p, hipStream_t s) {
   dim3 grid(p.R, p.Hkv, p.B);
-  if (q_dtype == kBF16)
+  if (p.sk_waves > 0) {
+    if (p.Dv > 512) return hipErrorInvalidValue;
+    dim3 ugrid(p.Hkv, p.B, (p.R + 3) / 4);
+    if (q_dtype == kBF16)
+      hipLaunchKernelGGL((combine_sk_kernel<kBF16>), ugrid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((combine_sk_kernel<kF16>), ugrid, dim3(256), 0, s, p);
+  } else if (q_dtype == kBF16) {
     hipLaunchKernelGGL((combine_kernel<kBF16>), grid, dim3(64), 0, s, p);
-  else
+  } else {
     hipLaunchKernelGGL((combine_kernel<kF16>), grid, dim3(64), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -30,6 +30,7 @@ struct Params {
   int B, Tq, Hq, Hkv, G, R, Dqk, Dv;
   int ps, pps, num_pages, window, mask_words16;
   int split_pages, max_splits;
+  int sk_waves;               // > 0: stream-K schedule over that many waves
   float qk_scale_log2;        // q_scale * kv_scale / sqrt(Dqk) * log2(e)
   float out_scale;            // kv_scale (V dequantisation, applied once)
 };
@@ -64,8 +65,115 @@ __device__ __forceinline__ SeqGeom seq_geom(const Params& p, int b) {
   }
   g.p0 = lo / p.ps;
   g.npages = (g.L + p.ps - 1) / p.ps - g.p0;
-  g.nsplits = (g.npages + p.split_pages - 1) / p.split_pages;
+  g.nsplits = p.split_pages > 0 ? (g.npages + p.split_pages - 1) / p.split_pages : 0;
   return g;
+}
+
+// ------------------------------------------------------- stream-K schedule
+// The 16-token tiles a sequence's query rows can see, [tile0, tile0 + ntiles).
+__device__ __forceinline__ int seq_tiles(const Params& p, int b, int* tile0) {
+  const SeqGeom g = seq_geom(p, b);
+  *tile0 = g.lo >> 4;
+  return g.L > g.lo ? ((g.L + 15) >> 4) - (g.lo >> 4) : 0;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Stream-K tile space: unit (b, kvh) owns the visible tiles of sequence b
+// for KV head kvh; units are laid end to end in (b, kvh) order, so unit
+// (b, kvh) starts at Hkv * pre_b + kvh * n_b with pre_b the tiles of the
+// sequences before b.  Wave w of W takes tiles [w T / W, (w+1) T / W).
+// Lane l holds pre_b and n_b of sequences b = l + 64 c (c < 4: B <= 256).
+constexpr int kSkMaxBatch = 256;
+struct SkSched {
+  int64_t T;     // total tiles
+  int pre[4];    // exclusive prefix of tiles per sequence (lane's sequences)
+  int cnt[4];    // tiles per sequence
+};
+
+__device__ __forceinline__ SkSched sk_schedule(const Params& p) {
+  SkSched s;
+  const int lane = threadIdx.x & 63;
+  int carry = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int b = lane + 64 * c;
+    int t0;
+    const int n = (64 * c < p.B && b < p.B) ? seq_tiles(p, b, &t0) : 0;
+    const int inc = wave_scan(n) + carry;
+    s.pre[c] = inc - n;
+    s.cnt[c] = n;
+    carry = __builtin_amdgcn_readlane(inc, 63);
+  }
+  s.T = (int64_t)carry * p.Hkv;
+  return s;
+}
+
+// Waves that get work: at most one per 8 tiles, so every wave with work has
+// at least 8 tiles (and none in 0 .. W_eff-1 is empty); the rest exit.
+__device__ __forceinline__ int sk_waves_eff(int64_t T, int W) {
+  const int64_t cap = T / 8 > 0 ? T / 8 : 1;
+  return (int)(cap < W ? cap : W);
+}
+
+// First tile of wave w of W: floor(w T / W).
+__device__ __forceinline__ int64_t sk_wave_start(int64_t T, int w, int W) {
+  return (T * (int64_t)w) / W;
+}
+
+// The wave whose range holds global tile x: the largest w with start(w) <= x.
+__device__ __forceinline__ int sk_wave_of(int64_t T, int64_t x, int W) {
+  return (int)(((x + 1) * (int64_t)W + T - 1) / T) - 1;
+}
+
+// Unit holding global tile x (x < T): sequence b, KV head kvh, its first
+// global tile, and its tile count.  Wave-uniform.
+struct SkUnit {
+  int b, kvh, ntiles;
+  int64_t start;
+};
+
+// pre_b and n_b of sequence b (wave-uniform b): read every chunk's lane and
+// select on the scalar side, so the per-lane arrays are never indexed
+// dynamically (which would put them in scratch memory).
+__device__ __forceinline__ void sk_seq_of(const SkSched& s, int b, int* pre, int* n) {
+  const int ln = b & 63, c = b >> 6;
+  const int p0 = __builtin_amdgcn_readlane(s.pre[0], ln), p1 = __builtin_amdgcn_readlane(s.pre[1], ln);
+  const int p2 = __builtin_amdgcn_readlane(s.pre[2], ln), p3 = __builtin_amdgcn_readlane(s.pre[3], ln);
+  const int n0 = __builtin_amdgcn_readlane(s.cnt[0], ln), n1 = __builtin_amdgcn_readlane(s.cnt[1], ln);
+  const int n2 = __builtin_amdgcn_readlane(s.cnt[2], ln), n3 = __builtin_amdgcn_readlane(s.cnt[3], ln);
+  *pre = c == 0 ? p0 : c == 1 ? p1 : c == 2 ? p2 : p3;
+  *n = c == 0 ? n0 : c == 1 ? n1 : c == 2 ? n2 : n3;
+}
+
+__device__ __forceinline__ SkUnit sk_locate(const Params& p, const SkSched& s, int64_t x) {
+  // last sequence whose first tile is <= x (it has tiles, since x < T)
+  int best = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int b = (threadIdx.x & 63) + 64 * c;
+    const bool ok = b < p.B && (int64_t)s.pre[c] * p.Hkv <= x;
+    const uint64_t m = __ballot(ok);
+    if (m != 0) best = 64 * c + 63 - __builtin_clzll(m);
+  }
+  SkUnit u;
+  u.b = best;
+  int pre, n;
+  sk_seq_of(s, best, &pre, &n);
+  const int64_t off = x - (int64_t)pre * p.Hkv;
+  u.kvh = (int)(off / n);
+  u.ntiles = n;
+  u.start = (int64_t)pre * p.Hkv + (int64_t)u.kvh * n;
+  return u;
 }
 
 // ---------------------------------------------------------------- vectors

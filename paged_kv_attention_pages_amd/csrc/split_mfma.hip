@@ -176,88 +176,96 @@ __device__ __forceinline__ void compute_tile(const Params& p, const SeqGeom& sg,
   }
 }
 
-}  // namespace
+// Everything one wave needs to stream a run of tiles of one (sequence, KV
+// head) unit and to finish it.
+template <int KT, int D>
+struct Unit {
+  static constexpr int KSTEPS = D / 32;
+  SeqGeom sg;
+  RowVis vis;
+  int b, kvh, lo_last, mask_from;
+  bool row_ok;
+  uint4 qb[KSTEPS];
+};
 
+template <int KT, int D>
+__device__ __forceinline__ void setup_unit(const Params& p, int b, int kvh, Unit<KT, D>& U) {
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  U.b = b;
+  U.kvh = kvh;
+  U.sg = seq_geom(p, b);
+  // Q^T operand of row n (zero rows pad the group to 16)
+  U.row_ok = n < p.R;
+  const uint16_t* qrow = (const uint16_t*)p.q + q_row_offset(p, b, kvh, U.row_ok ? n : 0) * p.Dqk;
+#pragma unroll
+  for (int s = 0; s < Unit<KT, D>::KSTEPS; ++s)
+    U.qb[s] = U.row_ok ? *(const uint4*)(qrow + qk_chunk<KT>(s, g) * 8) : make_uint4(0, 0, 0, 0);
+  U.vis = row_vis(p, b, U.sg.L, U.row_ok ? n : 0);
+  // tiles wholly inside [lo_last_row, mask_from) need no per-element test
+  U.lo_last = p.window > 0 ? U.sg.L - p.window : INT32_MIN;
+  U.mask_from = (p.Tq > 1 && p.mask != nullptr) ? U.sg.L - p.Tq : U.sg.L;
+}
+
+// Stream the sequence tiles [tile_from, tile_to) of the unit into A.  Runs of
+// at most 64 pages share one vector load of their page ids (one per lane);
+// each run goes through the NS-stage pipeline.
 template <int QT, int KT, int D>
-__global__ __launch_bounds__(64) void split_mfma16_kernel(Params p) {
+__device__ __forceinline__ void stream_tiles(const Params& p, const Unit<KT, D>& U, int tile_from,
+                                             int tile_to, Acc<D>& A) {
   using TT = Tile<KT, D>;
-  constexpr int KSTEPS = TT::KSTEPS, DT = TT::DT;
-
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const SeqGeom sg = seq_geom(p, b);
-  if (split >= sg.nsplits) return;
-  const int lane = threadIdx.x;
-  const int n = lane & 15, g = lane >> 4;
-
-  const int pg_begin = sg.p0 + split * p.split_pages;
-  const int pg_end = min(pg_begin + p.split_pages, sg.p0 + sg.npages);
-  const int tok_begin = max(pg_begin * p.ps, sg.lo);
-  const int tok_end = min(pg_end * p.ps, sg.L);
-  const int tile_begin = tok_begin >> 4, tile_end = (tok_end + 15) >> 4;
-
+  constexpr int NS = TT::STAGES, DT = TT::DT;
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const int tiles_per_page = p.ps >> 4;
   Stream st;
-  st.pg_begin = pg_begin;
-  st.tile_end = tile_end;
-  st.my_page = lane < pg_end - pg_begin ? p.page_table[(int64_t)b * p.pps + pg_begin + lane] : -1;
-  st.k_lane = (int)((n * p.k_slot + kvh * p.k_head) * TT::ELEM) + 16 * g;
-  st.v_lane = (int)((4 * g * p.v_slot + kvh * p.v_head + (int64_t)DT * n) * TT::ELEM);
+  st.k_lane = (int)((n * p.k_slot + U.kvh * p.k_head) * TT::ELEM) + 16 * g;
+  st.v_lane = (int)((4 * g * p.v_slot + U.kvh * p.v_head + (int64_t)DT * n) * TT::ELEM);
   st.k_page_bytes = (uint32_t)(p.k_page * TT::ELEM);
   st.v_page_bytes = (uint32_t)(p.v_page * TT::ELEM);
-
-  // Q^T operand of row n (zero rows pad the group to 16)
-  const bool row_ok = n < p.R;
-  uint4 qb[KSTEPS];
-  {
-    const uint16_t* qrow =
-        (const uint16_t*)p.q + q_row_offset(p, b, kvh, row_ok ? n : 0) * p.Dqk;
+  for (int run = tile_from; run < tile_to;) {
+    st.pg_begin = run / tiles_per_page;
+    const int run_end = min(tile_to, (st.pg_begin + 64) * tiles_per_page);
+    const int pg_last = (run_end - 1) / tiles_per_page;
+    st.tile_end = run_end;
+    st.my_page = lane <= pg_last - st.pg_begin
+                     ? p.page_table[(int64_t)U.b * p.pps + st.pg_begin + lane] : -1;
+    TT buf[NS];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-      qb[s] = row_ok ? *(const uint4*)(qrow + qk_chunk<KT>(s, g) * 8) : make_uint4(0, 0, 0, 0);
-  }
-  const RowVis vis = row_vis(p, b, sg.L, row_ok ? n : 0);
-  // tiles wholly inside [lo_last_row, mask_from) need no per-element test
-  const int lo_last = p.window > 0 ? sg.L - p.window : INT32_MIN;
-  const int mask_from = (p.Tq > 1 && p.mask != nullptr) ? sg.L - p.Tq : sg.L;
-
-  Acc<D> A;
-  A.m = kNegInf;
-  A.l = 0.f;
-#pragma unroll
-  for (int j = 0; j < DT; ++j) A.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // NS-stage pipeline: tiles t+1 .. t+NS-1 are in flight while t is computed.
-  // The scheduling barriers keep tile t's loads ahead of tile t+1's, so the
-  // wait before computing tile t leaves the younger tiles in flight.
-  constexpr int NS = TT::STAGES;
-  TT buf[NS];
-#pragma unroll
-  for (int k = 0; k < NS - 1; ++k) {
-    load_tile<KT, D>(p, st, tile_begin + k, buf[k]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  for (int t = tile_begin; t < tile_end; t += NS) {
-#pragma unroll
-    for (int k = 0; k < NS; ++k) {
-      load_tile<KT, D>(p, st, t + k + NS - 1, buf[(k + NS - 1) % NS]);
-      if (k == 0 || t + k < tile_end)
-        compute_tile<QT, KT, D>(p, sg, vis, lo_last, mask_from, qb, g, t + k, buf[k], A);
+    for (int k = 0; k < NS - 1; ++k) {
+      load_tile<KT, D>(p, st, run + k, buf[k]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    for (int t = run; t < run_end; t += NS) {
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        load_tile<KT, D>(p, st, t + k + NS - 1, buf[(k + NS - 1) % NS]);
+        if (k == 0 || t + k < run_end)
+          compute_tile<QT, KT, D>(p, U.sg, U.vis, U.lo_last, U.mask_from, U.qb, g, t + k, buf[k], A);
+      }
+    }
+    run = run_end;
   }
+}
 
-  // ---- epilogue: partial (m, l, o) to the workspace, or the output itself
+// Finish a unit: the normalised output when this wave saw all of it
+// (complete), else the partial (m, l, o) in workspace row `prow`.
+template <int QT, int KT, int D>
+__device__ __forceinline__ void finish_unit(const Params& p, const Unit<KT, D>& U, Acc<D>& A,
+                                            bool complete, int64_t prow) {
+  constexpr int DT = D / 16;
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const float l = sum_across_rows(A.l);
-  if (!row_ok) return;
+  if (!U.row_ok) return;
   // lane (n, g) holds dims DT*(4g+i) + j of row n
-  if (sg.nsplits == 1) {
+  if (complete) {
     float num = 1.f, den = l;
     if (p.sinks != nullptr) {
-      const float sk = p.sinks[kvh * p.G + n % p.G] * kLog2e;
+      const float sk = p.sinks[U.kvh * p.G + n % p.G] * kLog2e;
       const float Mf = fmaxf(A.m, sk);
       num = A.m == kNegInf ? 0.f : exp2f(A.m - Mf);
       den = l * num + exp2f(sk - Mf);
     }
     const float inv = den > 0.f ? p.out_scale * num / den : 0.f;
-    uint16_t* o = (uint16_t*)p.out + q_row_offset(p, b, kvh, n) * p.Dv;
+    uint16_t* o = (uint16_t*)p.out + q_row_offset(p, U.b, U.kvh, n) * p.Dv;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -266,7 +274,6 @@ __global__ __launch_bounds__(64) void split_mfma16_kernel(Params p) {
             make_uint2(pack2<QT>(A.o[j][i] * inv, A.o[j + 1][i] * inv),
                        pack2<QT>(A.o[j + 2][i] * inv, A.o[j + 3][i] * inv));
   } else {
-    const int64_t prow = (((int64_t)b * p.Hkv + kvh) * p.max_splits + split) * p.R + n;
     float* o = p.ws_o + prow * p.Dv;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -278,15 +285,76 @@ __global__ __launch_bounds__(64) void split_mfma16_kernel(Params p) {
   }
 }
 
+template <int D>
+__device__ __forceinline__ void reset(Acc<D>& A) {
+  A.m = kNegInf;
+  A.l = 0.f;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) A.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+}  // namespace
+
+// Grid schedule: one wave per (split, KV head, sequence); a split is
+// `split_pages` pages of the sequence's visible span.
+template <int QT, int KT, int D>
+__global__ __launch_bounds__(64) void split_mfma16_kernel(Params p) {
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const SeqGeom sg = seq_geom(p, b);
+  if (split >= sg.nsplits) return;
+  const int pg_begin = sg.p0 + split * p.split_pages;
+  const int pg_end = min(pg_begin + p.split_pages, sg.p0 + sg.npages);
+  const int tile_begin = max(pg_begin * p.ps, sg.lo) >> 4;
+  const int tile_end = (min(pg_end * p.ps, sg.L) + 15) >> 4;
+  Unit<KT, D> U;
+  setup_unit<KT, D>(p, b, kvh, U);
+  Acc<D> A;
+  reset<D>(A);
+  stream_tiles<QT, KT, D>(p, U, tile_begin, tile_end, A);
+  const int64_t prow = (((int64_t)b * p.Hkv + kvh) * p.max_splits + split) * p.R + (threadIdx.x & 15);
+  finish_unit<QT, KT, D>(p, U, A, sg.nsplits == 1, prow);
+}
+
+// Stream-K schedule: wave w of W takes an equal share of the tile stream of
+// all units; units wholly inside its share are finished here, the first and
+// the last (when cut) leave partials in workspace slots 2w and 2w+1.
+template <int QT, int KT, int D>
+__global__ __launch_bounds__(64) void split_mfma16_sk_kernel(Params p) {
+  const SkSched S = sk_schedule(p);
+  const int w = blockIdx.x, W = sk_waves_eff(S.T, gridDim.x);
+  if (w >= W) return;
+  const int64_t x0 = sk_wave_start(S.T, w, W), x1 = sk_wave_start(S.T, w + 1, W);
+  Unit<KT, D> U;
+  Acc<D> A;
+  for (int64_t x = x0; x < x1;) {
+    const SkUnit u = sk_locate(p, S, x);
+    const int64_t seg_end = min(x1, u.start + u.ntiles);
+    setup_unit<KT, D>(p, u.b, u.kvh, U);
+    reset<D>(A);
+    int tile0;
+    seq_tiles(p, u.b, &tile0);
+    stream_tiles<QT, KT, D>(p, U, tile0 + (int)(x - u.start), tile0 + (int)(seg_end - u.start), A);
+    const bool complete = x == u.start && seg_end == u.start + u.ntiles;
+    const int slot = 2 * w + (x == x0 ? 0 : 1);
+    finish_unit<QT, KT, D>(p, U, A, complete, (int64_t)slot * p.R + (threadIdx.x & 15));
+    x = seg_end;
+  }
+}
+
 template <int QT, int KT, int D>
 hipError_t launch_split_mfma16(const Params& p, hipStream_t stream) {
-  dim3 grid(p.max_splits, p.Hkv, p.B);
-  hipLaunchKernelGGL((split_mfma16_kernel<QT, KT, D>), grid, dim3(64), 0, stream, p);
+  if (p.sk_waves > 0) {
+    hipLaunchKernelGGL((split_mfma16_sk_kernel<QT, KT, D>), dim3(p.sk_waves), dim3(64), 0, stream, p);
+  } else {
+    dim3 grid(p.max_splits, p.Hkv, p.B);
+    hipLaunchKernelGGL((split_mfma16_kernel<QT, KT, D>), grid, dim3(64), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_split_mfma16(int q_dtype, int kv_dtype, int D, const Params& p, hipStream_t s) {
-  if (p.split_pages > 64) return hipErrorInvalidValue;
+  if (p.sk_waves == 0 && p.split_pages > 64) return hipErrorInvalidValue;
+  if (p.sk_waves > 0 && p.B > kSkMaxBatch) return hipErrorInvalidValue;
 #define PKV_CASE(QT, KT, DD) \
   if (q_dtype == QT && kv_dtype == KT && D == DD) return launch_split_mfma16<QT, KT, DD>(p, s);
   PKV_CASE(kBF16, kBF16, 128)

@@ -99,9 +99,19 @@ def test_plan_paths():
 def test_plan_window_bounds_splits():
     # a 4096-token window over 32-token pages touches at most 129 pages
     p = plan(batch=128, num_q_heads=64, kv_dtype=torch.float8_e4m3fn, page_size=32,
-             pages_per_seq=1024, window=4096)
+             pages_per_seq=1024, window=4096, path="valu")
     assert p["split_pages"] * p["max_splits"] >= 129
     assert (p["max_splits"] - 1) * p["split_pages"] < 129
+
+
+def test_plan_stream_k():
+    # default matrix-core plan: persistent waves, 4 per CU, two partial slots each
+    p = plan()
+    assert p["split_pages"] == 0 and p["ctas_per_split_grid"] == 4 * 256
+    assert p["workspace_bytes"] >= 2 * 1024 * 4 * (128 * 4 + 8)
+    assert plan(target_ctas=100)["ctas_per_split_grid"] == 100
+    # batches above 256 fall back to the grid schedule
+    assert plan(batch=300)["split_pages"] > 0
 
 
 def test_plan_forced_split_and_workspace():
@@ -118,7 +128,7 @@ def test_plan_forced_split_and_workspace():
 
 def test_plan_split_sizes_multiple_of_pages_and_at_least_256_tokens():
     for ps in (16, 32, 64, 128):
-        p = plan(page_size=ps, pages_per_seq=8192 // ps)
+        p = plan(page_size=ps, pages_per_seq=8192 // ps, path="valu")
         assert p["split_pages"] * ps >= 256
         assert p["split_pages"] * p["max_splits"] >= 8192 // ps
 

@@ -363,3 +363,28 @@ def test_visible_sets_exact(case):
     vis_ref = ref > 0
     assert torch.equal(vis_got, vis_ref), f"visible sets differ at {torch.nonzero(vis_got != vis_ref)[:8].tolist()}"
     torch.testing.assert_close(got.double(), ref, rtol=2 ** -7, atol=0)
+
+
+# ---------------------------------------------------------------- stream-K schedule
+
+@pytest.mark.parametrize("W", [1, 3, 7, 64, 5000])
+@pytest.mark.parametrize("name", ["gqa", "fp8", "spec", "tiny"])
+def test_stream_k_wave_counts(name, W):
+    # 1 wave finishes every unit itself; 3 and 7 cut units across many waves;
+    # 5000 waves exceed the tile count, so most waves are empty
+    w = SMALL[name]
+    print(f"[case] stream-K {name} waves={W}", flush=True)
+    inp = make(w, seed=70)
+    got = run_gpu(w, inp, target_ctas=W)
+    assert_parity(w, got, run_oracle(w, inp), f"sk/{name}/W{W}")
+
+
+def test_stream_k_empty_sequences_and_split_invariance():
+    w = SMALL["gqa"].replace(batch=8)
+    lens = [0, 1, 15, 0, 17, 63, 1023, 0]
+    inp = make(w, seed=71, seq_lens=lens)
+    ref = run_oracle(w, inp)
+    outs = [run_gpu(w, inp, target_ctas=W) for W in (1, 5, 37, 2048)]
+    for o in outs:
+        assert_parity(w, o, ref, "sk-empty")
+        assert torch.equal(o[0].float().cpu(), torch.zeros_like(o[0].float().cpu()))
