@@ -169,10 +169,13 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
   pl->num_cus = cus;
   pl->sk_waves = 0;
   // Stream-K schedule (matrix-core path, batch <= 256, no forced split size):
-  // four persistent waves per CU (measured best: one per SIMD, each with a
-  // three-stage pipeline in flight); 2 partial slots per wave.
+  // persistent waves (measured best: one per SIMD for 16-bit caches, each
+  // with a three-stage pipeline in flight); 2 partial slots per wave.
   if (path == PKV_PATH_MFMA && d->batch <= 256 && !(opts && opts->split_pages > 0)) {
-    const int64_t W = (opts && opts->target_ctas > 0) ? opts->target_ctas : 4LL * cus;
+    // fp8 tiles carry half the bytes for the same matrix work, so more waves
+    // per CU hide the conversion work: 8 per CU for fp8, 4 for 16-bit caches
+    const int64_t per_cu = d->kv_dtype == PKV_FP8_E4M3 ? 8 : 4;
+    const int64_t W = (opts && opts->target_ctas > 0) ? opts->target_ctas : per_cu * cus;
     pl->sk_waves = (int)std::min<int64_t>(W, 1 << 20);
     pl->split_pages = 0;
     pl->max_splits = 0;

@@ -142,37 +142,41 @@ __device__ __forceinline__ void compute_tile(const Params& p, const SeqGeom& sg,
   tmax = max_across_rows(tmax);
   const float m_new = fmaxf(A.m, tmax);
   const float m_ref = m_new == kNegInf ? 0.f : m_new;
-  const float alpha = exp2f(A.m - m_ref);
+  // raw v_exp_f32: every argument is <= 0 (or -inf), and weights below the
+  // fp32 normal range may flush to zero without changing the result
+  const float alpha = __builtin_amdgcn_exp2f(A.m - m_ref);
   float pr[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pr[i] = exp2f(x[i] - m_ref);
+  for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
   A.l = A.l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
   A.m = m_new;
+  // the running max rarely rises after the first tiles: rescale only then
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-  for (int j = 0; j < DT; ++j) A.o[j] *= alpha;
+    for (int j = 0; j < DT; ++j) A.o[j] *= alpha;
+  }
   const uint2 pb = make_uint2(pack2<QT>(pr[0], pr[1]), pack2<QT>(pr[2], pr[3]));
   // ---- O^T += V^T . P^T
-  uint32_t v16[4][DT / 2];
+  // operand of dim j: element j of the lane's V chunk for its four tokens
+  if constexpr (KT == kFP8) {
+    // gather byte j of the four tokens into one word, convert the four at
+    // once (exact), and keep them in token order
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    if constexpr (KT == kFP8) {
-#pragma unroll
-      for (int w = 0; w < TT::VW; ++w) {
-        const uint2 c = fp8x4_to_16<QT>(T.v[kk][w]);
-        v16[kk][2 * w] = c.x;
-        v16[kk][2 * w + 1] = c.y;
-      }
-    } else {
-#pragma unroll
-      for (int w = 0; w < DT / 2; ++w) v16[kk][w] = T.v[kk][w];
+    for (int j = 0; j < DT; ++j) {
+      const int wi = j >> 2, b = j & 3;
+      const uint32_t p01 = __builtin_amdgcn_perm(T.v[1][wi], T.v[0][wi], 0x0c0c0400u | (b << 8) | b);
+      const uint32_t p23 = __builtin_amdgcn_perm(T.v[3][wi], T.v[2][wi], 0x04000c0cu | (b << 24) | (b << 16));
+      const uint2 a = fp8x4_to_16<QT>(p01 | p23);
+      A.o[j] = mfma_k16<QT>(a, pb, A.o[j]);
     }
-  }
+  } else {
 #pragma unroll
-  for (int j = 0; j < DT; ++j) {
-    const int sh = 16 * (j & 1);
-    const uint32_t e0 = (v16[0][j >> 1] >> sh) & 0xffffu, e1 = (v16[1][j >> 1] >> sh) & 0xffffu;
-    const uint32_t e2 = (v16[2][j >> 1] >> sh) & 0xffffu, e3 = (v16[3][j >> 1] >> sh) & 0xffffu;
-    A.o[j] = mfma_k16<QT>(make_uint2(e0 | (e1 << 16), e2 | (e3 << 16)), pb, A.o[j]);
+    for (int j = 0; j < DT; ++j) {
+      const int sh = 16 * (j & 1);
+      const uint32_t e0 = (T.v[0][j >> 1] >> sh) & 0xffffu, e1 = (T.v[1][j >> 1] >> sh) & 0xffffu;
+      const uint32_t e2 = (T.v[2][j >> 1] >> sh) & 0xffffu, e3 = (T.v[3][j >> 1] >> sh) & 0xffffu;
+      A.o[j] = mfma_k16<QT>(make_uint2(e0 | (e1 << 16), e2 | (e3 << 16)), pb, A.o[j]);
+    }
   }
 }
 
@@ -319,7 +323,9 @@ __global__ __launch_bounds__(64) void split_mfma16_kernel(Params p) {
 // all units; units wholly inside its share are finished here, the first and
 // the last (when cut) leave partials in workspace slots 2w and 2w+1.
 template <int QT, int KT, int D>
-__global__ __launch_bounds__(64) void split_mfma16_sk_kernel(Params p) {
+// (two waves per SIMD: the register budget keeps the accumulators in
+// architected VGPRs instead of moving them through AGPRs every tile)
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma16_sk_kernel(Params p) {
   const SkSched S = sk_schedule(p);
   const int w = blockIdx.x, W = sk_waves_eff(S.T, gridDim.x);
   if (w >= W) return;

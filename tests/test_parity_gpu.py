@@ -388,3 +388,34 @@ def test_stream_k_empty_sequences_and_split_invariance():
     for o in outs:
         assert_parity(w, o, ref, "sk-empty")
         assert torch.equal(o[0].float().cpu(), torch.zeros_like(o[0].float().cpu()))
+
+
+@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("W", [5, 0])
+def test_stream_k_other_head_dims(D, W):
+    w = SMALL["gqa"].replace(head_dim_qk=D, head_dim_v=D, batch=3, seq_len_range=(1, 600))
+    print(f"[case] stream-K head_dim {D} waves={W}", flush=True)
+    inp = make(w, seed=80 + D)
+    got = run_gpu(w, inp, target_ctas=W)
+    assert_parity(w, got, run_oracle(w, inp), f"sk-D{D}-W{W}")
+
+
+def test_repeated_calls_reuse_workspace():
+    # workspace contents on entry are arbitrary: a garbage-filled workspace,
+    # reused across calls, must give the same result every time
+    w = SMALL["spec"]
+    inp = make(w, seed=81)
+    ref = run_oracle(w, inp)
+    plan = pkv.query_plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                          head_dim_qk=128, head_dim_v=128, pages_per_seq=inp["page_table"].shape[1],
+                          page_size=w.page_size, q_seq_len=w.q_seq_len, target_ctas=7)
+    ws = torch.randint(0, 255, (plan["workspace_bytes"],), dtype=torch.uint8, device=DEV)
+    for _ in range(3):
+        out = torch.full((w.batch, w.q_seq_len, w.num_q_heads, 128), float("nan"),
+                         dtype=w.q_dtype, device=DEV)
+        pkv.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"],
+                        inp["seq_lens"], out, ws, num_kv_heads=w.num_kv_heads,
+                        page_size=w.page_size, kv_layout=w.kv_layout, q_seq_len=w.q_seq_len,
+                        mask=inp["mask"], target_ctas=7)
+        torch.cuda.synchronize()
+        assert_parity(w, out, ref, "ws-reuse")
