@@ -144,6 +144,9 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
   const int64_t units = (int64_t)d->batch * Hkv;
   const int64_t row_bytes = (int64_t)(Dk + (aliased ? 0 : Dv)) * kv_elem(d->kv_dtype);
   const int64_t page_bytes = (int64_t)ps * row_bytes;
+  // kernels address inside one page (all KV heads) with 32-bit byte offsets
+  if (page_bytes * Hkv >= (int64_t)1 << 31)
+    return fail(PKV_ERR_UNSUPPORTED, "one cache page (all KV heads) must be under 2 GiB");
   const int64_t partial_bytes = (int64_t)R * Dv * 4 + (int64_t)R * 8;
   // keep each split's partial-result traffic under ~1/8 of its cache bytes,
   // and every split at least 256 tokens long
@@ -171,10 +174,16 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
   // Stream-K schedule (matrix-core path, batch <= 256, no forced split size):
   // persistent waves (measured best: one per SIMD for 16-bit caches, each
   // with a three-stage pipeline in flight); 2 partial slots per wave.
-  if (path == PKV_PATH_MFMA && d->batch <= 256 && !(opts && opts->split_pages > 0)) {
+  // The latent-cache kernel runs the same schedule over 32-token tiles with
+  // one four-wave workgroup per CU (its register budget allows no more).
+  // (its 32-bit tile counters need the whole tile stream under 2^31 tiles)
+  const bool sk_path =
+      path == PKV_PATH_MFMA ||
+      (path == PKV_PATH_MFMA_MLA && units * cdiv(pps * ps, 32) < ((int64_t)1 << 31));
+  if (sk_path && d->batch <= 256 && !(opts && opts->split_pages > 0)) {
     // fp8 tiles carry half the bytes for the same matrix work, so more waves
     // per CU hide the conversion work: 8 per CU for fp8, 4 for 16-bit caches
-    const int64_t per_cu = d->kv_dtype == PKV_FP8_E4M3 ? 8 : 4;
+    const int64_t per_cu = path == PKV_PATH_MFMA_MLA ? 1 : d->kv_dtype == PKV_FP8_E4M3 ? 8 : 4;
     const int64_t W = (opts && opts->target_ctas > 0) ? opts->target_ctas : per_cu * cus;
     pl->sk_waves = (int)std::min<int64_t>(W, 1 << 20);
     pl->split_pages = 0;
@@ -261,6 +270,7 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
   p.split_pages = pl.split_pages;
   p.max_splits = pl.max_splits;
   p.sk_waves = pl.sk_waves;
+  p.sk_shift = pl.path == PKV_PATH_MFMA_MLA ? 5 : 4;
   p.qk_scale_log2 = (float)((double)q_scale * (double)kv_scale / std::sqrt((double)Dk) *
                             1.4426950408889634);
   p.out_scale = kv_scale;

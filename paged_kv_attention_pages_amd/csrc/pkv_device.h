@@ -31,6 +31,8 @@ struct Params {
   int ps, pps, num_pages, window, mask_words16;
   int split_pages, max_splits;
   int sk_waves;               // > 0: stream-K schedule over that many waves
+                              // (or workgroups, for the latent-cache kernel)
+  int sk_shift;               // stream-K tiles are 1 << sk_shift tokens
   float qk_scale_log2;        // q_scale * kv_scale / sqrt(Dqk) * log2(e)
   float out_scale;            // kv_scale (V dequantisation, applied once)
 };
@@ -70,11 +72,13 @@ __device__ __forceinline__ SeqGeom seq_geom(const Params& p, int b) {
 }
 
 // ------------------------------------------------------- stream-K schedule
-// The 16-token tiles a sequence's query rows can see, [tile0, tile0 + ntiles).
+// The stream-K tiles (1 << sk_shift tokens, aligned) that a sequence's query
+// rows can see, [tile0, tile0 + ntiles).
 __device__ __forceinline__ int seq_tiles(const Params& p, int b, int* tile0) {
   const SeqGeom g = seq_geom(p, b);
-  *tile0 = g.lo >> 4;
-  return g.L > g.lo ? ((g.L + 15) >> 4) - (g.lo >> 4) : 0;
+  const int sh = p.sk_shift, m = (1 << sh) - 1;
+  *tile0 = g.lo >> sh;
+  return g.L > g.lo ? ((g.L + m) >> sh) - (g.lo >> sh) : 0;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.

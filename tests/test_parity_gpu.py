@@ -419,3 +419,62 @@ def test_repeated_calls_reuse_workspace():
                         mask=inp["mask"], target_ctas=7)
         torch.cuda.synchronize()
         assert_parity(w, out, ref, "ws-reuse")
+
+
+# ---------------------------------------------------------------- latent (MLA) path
+
+MLA_SMALL = SMALL["mla"].replace(batch=3, seq_len_range=(1, 700))
+
+
+@pytest.mark.parametrize("ps", [16, 32, 64, 128])
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+@pytest.mark.parametrize("split", [0, 3])
+def test_mla_page_sizes_and_layouts(ps, layout, split):
+    # split 0: stream-K over 32-token tiles; split 3: grid schedule whose
+    # 3-page splits start mid-tile when the page holds 16 tokens
+    w = MLA_SMALL.replace(page_size=ps, kv_layout=layout)
+    print(f"[case] mla ps={ps} {layout} split={split}", flush=True)
+    inp = make(w, seed=90 + ps)
+    got = run_gpu(w, inp, split_pages=split)
+    assert_parity(w, got, run_oracle(w, inp), f"mla/ps{ps}/{layout}/split{split}")
+
+
+@pytest.mark.parametrize("variant", ["window_sinks", "f16", "rows20", "rows40", "spec2_random",
+                                     "spec4_causal"])
+@pytest.mark.parametrize("split", [0, 1])
+def test_mla_variants(variant, split):
+    w = {
+        "window_sinks": MLA_SMALL.replace(window=100, sinks=True, seq_len_range=(1, 900)),
+        "f16": MLA_SMALL.replace(q_dtype=torch.float16, kv_dtype=torch.float16),
+        "rows20": MLA_SMALL.replace(num_q_heads=20),
+        "rows40": MLA_SMALL.replace(num_q_heads=40, sinks=True),
+        "spec2_random": MLA_SMALL.replace(num_q_heads=32, q_seq_len=2, mask="random",
+                                          seq_len_range=(2, 700)),
+        "spec4_causal": MLA_SMALL.replace(num_q_heads=16, q_seq_len=4, mask="causal", window=40,
+                                          seq_len_range=(4, 700)),
+    }[variant]
+    print(f"[case] mla {variant} split={split}", flush=True)
+    inp = make(w, seed=95)
+    got = run_gpu(w, inp, split_pages=split)
+    assert_parity(w, got, run_oracle(w, inp), f"mla/{variant}/split{split}")
+
+
+def test_mla_empty_and_ragged_sequences():
+    w = MLA_SMALL.replace(batch=9)
+    lens = [0, 1, 31, 32, 33, 0, 64, 65, 700]
+    inp = make(w, seed=96, seq_lens=lens)
+    ref = run_oracle(w, inp)
+    for split, W in ((0, 0), (0, 5), (1, 0)):
+        got = run_gpu(w, inp, split_pages=split, target_ctas=W)
+        for b in (0, 5):
+            assert torch.equal(got[b].float().cpu(), torch.zeros_like(got[b].float().cpu()))
+        assert_parity(w, got, ref, f"mla-ragged/split{split}/W{W}")
+
+
+@pytest.mark.parametrize("W", [1, 3, 7, 64, 5000])
+def test_mla_stream_k_workgroup_counts(W):
+    w = MLA_SMALL
+    print(f"[case] mla stream-K workgroups={W}", flush=True)
+    inp = make(w, seed=97)
+    got = run_gpu(w, inp, target_ctas=W)
+    assert_parity(w, got, run_oracle(w, inp), f"mla-sk/W{W}")
