@@ -258,6 +258,26 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
   }
 }
 
+// The two 16-bit values of a packed pair, widened to fp32 (exact).
+template <int QT>
+__device__ __forceinline__ float2 unpack2(uint32_t w) {
+  if constexpr (QT == kBF16) {
+    return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+  } else {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 h = __builtin_bit_cast(f16x2, w);
+    return make_float2((float)h[0], (float)h[1]);
+  }
+}
+
+// Softmax reference slack (log2 units): a kernel moves its running
+// reference max only when a tile's max passes it by more than this, so the
+// probabilities stay below 2^kSlack -- held by bf16, f16 and the fp32
+// accumulators with unchanged relative precision -- and the accumulators
+// are rescaled far less often.  Normalisation and the split merge are exact
+// for any reference.
+constexpr float kSlack = 8.f;
+
 // Four OCP e4m3fn bytes -> four fp32 (exact).
 __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));

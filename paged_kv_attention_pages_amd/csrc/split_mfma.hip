@@ -140,22 +140,27 @@ __device__ __forceinline__ void compute_tile(const Params& p, const SeqGeom& sg,
   }
   float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
   tmax = max_across_rows(tmax);
-  const float m_new = fmaxf(A.m, tmax);
+  // the reference A.m moves only when the tile max passes it by kSlack
+  const bool bump = tmax > A.m + kSlack;
+  const float m_new = bump ? tmax : A.m;
   const float m_ref = m_new == kNegInf ? 0.f : m_new;
-  // raw v_exp_f32: every argument is <= 0 (or -inf), and weights below the
-  // fp32 normal range may flush to zero without changing the result
-  const float alpha = __builtin_amdgcn_exp2f(A.m - m_ref);
+  // raw v_exp_f32: every argument is <= kSlack (or -inf), and weights below
+  // the fp32 normal range may flush to zero without changing the result
+  const float alpha = bump ? __builtin_amdgcn_exp2f(A.m - m_ref) : 1.f;
   float pr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
-  A.l = A.l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+  // the sum takes the rounded probabilities that P . V uses, so the output
+  // is an exact weighted mean of the V rows
+  const uint2 pb = make_uint2(pack2<QT>(pr[0], pr[1]), pack2<QT>(pr[2], pr[3]));
+  const float2 r0 = unpack2<QT>(pb.x), r1 = unpack2<QT>(pb.y);
+  A.l = A.l * alpha + ((r0.x + r0.y) + (r1.x + r1.y));
   A.m = m_new;
-  // the running max rarely rises after the first tiles: rescale only then
+  // the reference rarely moves after the first tiles: rescale only then
   if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
     for (int j = 0; j < DT; ++j) A.o[j] *= alpha;
   }
-  const uint2 pb = make_uint2(pack2<QT>(pr[0], pr[1]), pack2<QT>(pr[2], pr[3]));
   // ---- O^T += V^T . P^T
   // operand of dim j: element j of the lane's V chunk for its four tokens
   if constexpr (KT == kFP8) {

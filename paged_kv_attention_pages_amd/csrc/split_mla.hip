@@ -189,11 +189,12 @@ __device__ __forceinline__ void compute_tile(const Params& p, const Piece& P, co
       for (int st = 0; st < 2; ++st) a = mfma_k32<QT>(T.k[tb][st], Q.k[rb][st], a);
       s[tb][rb] = a;
     }
+  // every partial goes through LDS (also the owner's own: uniform code, no
+  // branches, and the owner's eight reads issue back to back)
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-      if (rb != w) sm.s[rb][w][tb][lane] = s[tb][rb];
+    for (int rb = 0; rb < 4; ++rb) sm.s[rb][w][tb][lane] = s[tb][rb];
   lds_barrier();
 
   // ---- 2. waves 0..3: sum the eight partials of row block w; online softmax
@@ -212,41 +213,56 @@ __device__ __forceinline__ void compute_tile(const Params& p, const Piece& P, co
     f32x4 sc[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      f32x4 a = w == 0 ? s[tb][0] : w == 1 ? s[tb][1] : w == 2 ? s[tb][2] : s[tb][3];
+      // eight reads in flight, then a pairwise sum in a fixed order; one
+      // token block at a time to bound the registers held by the reads
+      f32x4 part[kWaves];
 #pragma unroll
-      for (int src = 0; src < kWaves; ++src)
-        if (src != w) a += sm.s[w][src][tb][lane];
-      sc[tb] = a;
+      for (int src = 0; src < kWaves; ++src) part[src] = sm.s[w][src][tb][lane];
+      const f32x4 a01 = part[0] + part[1], a23 = part[2] + part[3];
+      const f32x4 a45 = part[4] + part[5], a67 = part[6] + part[7];
+      sc[tb] = (a01 + a23) + (a45 + a67);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    const bool edge =
-        tok0 < max(P.tok_lo, P.lo_last) || tok0 + kTileTok > min(P.tok_hi, P.mask_from);
     float x[2][4];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = tok0 + 16 * tb + 4 * g + i;
-        const float xi = sc[tb][i] * p.qk_scale_log2;
-        const bool v = (tok >= P.tok_lo) & (tok < P.tok_hi) & P.vis(tok, P.L);
-        x[tb][i] = (!edge || v) ? xi : kNegInf;
-      }
+      for (int i = 0; i < 4; ++i) x[tb][i] = sc[tb][i] * p.qk_scale_log2;
+    // tiles that hold an invisible token for some row (window, draft mask,
+    // the ends of the piece) mask; the others are visible to every row
+    if (tok0 < max(P.tok_lo, P.lo_last) || tok0 + kTileTok > min(P.tok_hi, P.mask_from)) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = tok0 + 16 * tb + 4 * g + i;
+          const bool v = (tok >= P.tok_lo) & (tok < P.tok_hi) & P.vis(tok, P.L);
+          x[tb][i] = v ? x[tb][i] : kNegInf;
+        }
+    }
     float tmax = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
                        fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
     tmax = max_across_rows(tmax);
-    const float m_new = fmaxf(A.m, tmax);
+    // the reference A.m moves only when the tile max passes it by kSlack
+    const bool bump = tmax > A.m + kSlack;
+    const float m_new = bump ? tmax : A.m;
     const float m_ref = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(A.m - m_ref);
+    const float alpha = bump ? __builtin_amdgcn_exp2f(A.m - m_ref) : 1.f;
     float pr[2][4];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) pr[tb][i] = __builtin_amdgcn_exp2f(x[tb][i] - m_ref);
-    A.l = A.l * alpha + (((pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3])) +
-                         ((pr[1][0] + pr[1][1]) + (pr[1][2] + pr[1][3])));
-    A.m = m_new;
-    // P^T operand: K index 8 g + c <-> the token order used for vt
-    sm.pm[w][lane] = make_uint4(pack2<QT>(pr[0][0], pr[0][1]), pack2<QT>(pr[0][2], pr[0][3]),
+    // P^T operand (K index 8 g + c <-> the token order used for vt); the sum
+    // takes the rounded probabilities, so the output is an exact weighted
+    // mean of the V rows and the rounding error scales with |V - out|
+    const uint4 pw = make_uint4(pack2<QT>(pr[0][0], pr[0][1]), pack2<QT>(pr[0][2], pr[0][3]),
                                 pack2<QT>(pr[1][0], pr[1][1]), pack2<QT>(pr[1][2], pr[1][3]));
+    const float2 r0 = unpack2<QT>(pw.x), r1 = unpack2<QT>(pw.y);
+    const float2 r2 = unpack2<QT>(pw.z), r3 = unpack2<QT>(pw.w);
+    A.l = A.l * alpha + (((r0.x + r0.y) + (r1.x + r1.y)) + ((r2.x + r2.y) + (r3.x + r3.y)));
+    A.m = m_new;
+    sm.pm[w][lane] = pw;
     if (g == 0) sm.alpha[n][w] = alpha;
   }
   lds_barrier();
