@@ -312,17 +312,32 @@ __device__ __forceinline__ uint32_t half_of(const uint4& v, int e) {
 }
 
 // Butterfly max across the four 16-lane rows of a wave (lanes l, l^16,
-// l^32, l^48): every lane ends with the max of its column.
+// l^32, l^48): every lane ends with the max of its column.  gfx950's
+// v_permlane16_swap / v_permlane32_swap exchange 16-lane rows and 32-lane
+// halves between two registers in the VALU; with the value in both
+// operands, each lane ends up holding itself in one result and its partner
+// (l ^ 16, resp. l ^ 32) in the other, so no LDS round trip is needed.
+__device__ __forceinline__ float2 row_partner16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float2 row_partner32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float max_across_rows(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  float2 a = row_partner16(x);
+  x = fmaxf(a.x, a.y);
+  a = row_partner32(x);
+  return fmaxf(a.x, a.y);
 }
 
 __device__ __forceinline__ float sum_across_rows(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  float2 a = row_partner16(x);
+  x = a.x + a.y;
+  a = row_partner32(x);
+  return a.x + a.y;
 }
 
 // Row r of the (G * Tq) rows sharing one KV head: query token r / G, head

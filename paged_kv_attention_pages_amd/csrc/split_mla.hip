@@ -54,11 +54,13 @@ constexpr int kTileShift = 5;
 constexpr int kRowChunks = kVw / 8 + 1;       // staged token row: 8 chunks + 1 pad chunk
 static_assert(kVw == 64 && kRw == 8, "dimension split assumes the 576/512 latent row");
 
+// Staging, P and the rescale factors are double-buffered by tile parity:
+// tile t's P . V runs while tile t + 1's softmax is computed.
 struct Smem {
-  uint4 t[kWaves][kTileTok * kRowChunks];     // per-wave staging for the V transpose
+  uint4 t[2][kWaves][kTileTok * kRowChunks];  // per-wave staging for the V transpose
   f32x4 s[4][kWaves][2][64];                  // partial scores [row block][from wave][token block]
-  uint4 pm[4][64];                            // P^T operand of each row block
-  float alpha[16][4];                         // rescale factor of row 16 rb + n at [n][rb]
+  uint4 pm[2][4][64];                         // P^T operand of each row block
+  float alpha[2][16][4];                      // rescale factor of row 16 rb + n at [n][rb]
   float2 ml[64];                              // (max, sum) per row at the end of a unit
 };
 
@@ -167,14 +169,59 @@ __device__ __forceinline__ void load_tile(const Params& p, const Piece& P, int m
   }
 }
 
+// O^T += V^T . P^T for the tile staged in buffer `buf`, after rescaling the
+// accumulators by that tile's factors.  Every wave, its own 64 dims.
+template <int QT>
+__device__ __forceinline__ void pv_tile(int buf, Smem& sm, Acc& A) {
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4, w = wave_id();
+  // V^T operand source: token sigma(8 g + c) of this wave's block, dims 4 n .. 4 n + 4,
+  // where the MFMA K index 8 g + c maps to token 4 g + c (c < 4) or 16 + 4 g + c - 4
+  const uint2* rows2 = (const uint2*)sm.t[buf][w];
+  uint2 vt[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int tk = c < 4 ? 4 * g + c : 16 + 4 * g + (c - 4);
+    vt[c] = rows2[tk * (2 * kRowChunks) + n];
+  }
+  uint4 pb[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) pb[rb] = sm.pm[buf][rb][lane];
+  const float4 al = *(const float4*)&sm.alpha[buf][n][0];
+  const float alr[4] = {al.x, al.y, al.z, al.w};
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+    if (__builtin_amdgcn_ballot_w64(alr[rb] != 1.f) != 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) A.o[rb][e] *= alr[rb];
+    }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    // 16-bit element e of each staged chunk, two tokens per dword
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t a[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = (e >> 1) ? vt[2 * q].y : vt[2 * q].x;
+      const uint32_t hi = (e >> 1) ? vt[2 * q + 1].y : vt[2 * q + 1].x;
+      a[q] = __builtin_amdgcn_perm(hi, lo, sel);
+    }
+    const uint4 av = make_uint4(a[0], a[1], a[2], a[3]);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) A.o[rb][e] = mfma_k32<QT>(av, pb[rb], A.o[rb][e]);
+  }
+}
+
+// Tile t: scores and softmax of t, and P . V of the previous tile (pv_prev)
+// next to this tile's score product.
 template <int QT>
 __device__ __forceinline__ void compute_tile(const Params& p, const Piece& P, const QRegs& Q,
-                                             const KTile& T, int t, Smem& sm, Acc& A) {
+                                             const KTile& T, int t, bool pv_prev, Smem& sm, Acc& A) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4, w = wave_id();
   const int tok0 = t * kTileTok;
+  const int cur = t & 1;
 
   // ---- 1. partial scores over this wave's dims; stage the tile for the transpose
-  uint4* st_rows = sm.t[w];
+  uint4* st_rows = sm.t[cur][w];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -195,20 +242,13 @@ __device__ __forceinline__ void compute_tile(const Params& p, const Piece& P, co
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) sm.s[rb][w][tb][lane] = s[tb][rb];
+  // ---- the previous tile's O^T += V^T . P^T: its staging, P and factors
+  // were published by the previous step's barriers, and running it here
+  // keeps the matrix cores busy while the LDS absorbs this tile's writes
+  if (pv_prev) pv_tile<QT>(cur ^ 1, sm, A);
   lds_barrier();
 
   // ---- 2. waves 0..3: sum the eight partials of row block w; online softmax
-  // V^T operand source: token sigma(8 g + c) of this wave's block, dims 4 n .. 4 n + 4,
-  // where the MFMA K index 8 g + c maps to token 4 g + c (c < 4) or 16 + 4 g + c - 4
-  uint2 vt[8];
-  {
-    const uint2* rows2 = (const uint2*)st_rows;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int tk = c < 4 ? 4 * g + c : 16 + 4 * g + (c - 4);
-      vt[c] = rows2[tk * (2 * kRowChunks) + n];
-    }
-  }
   if (w < 4) {
     f32x4 sc[2];
 #pragma unroll
@@ -253,47 +293,19 @@ __device__ __forceinline__ void compute_tile(const Params& p, const Piece& P, co
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) pr[tb][i] = __builtin_amdgcn_exp2f(x[tb][i] - m_ref);
-    // P^T operand (K index 8 g + c <-> the token order used for vt); the sum
-    // takes the rounded probabilities, so the output is an exact weighted
-    // mean of the V rows and the rounding error scales with |V - out|
+    // P^T operand (K index 8 g + c <-> the token order of the V^T operand);
+    // the sum takes the rounded probabilities, so the output is an exact
+    // weighted mean of the V rows and the rounding error scales with |V - out|
     const uint4 pw = make_uint4(pack2<QT>(pr[0][0], pr[0][1]), pack2<QT>(pr[0][2], pr[0][3]),
                                 pack2<QT>(pr[1][0], pr[1][1]), pack2<QT>(pr[1][2], pr[1][3]));
     const float2 r0 = unpack2<QT>(pw.x), r1 = unpack2<QT>(pw.y);
     const float2 r2 = unpack2<QT>(pw.z), r3 = unpack2<QT>(pw.w);
     A.l = A.l * alpha + (((r0.x + r0.y) + (r1.x + r1.y)) + ((r2.x + r2.y) + (r3.x + r3.y)));
     A.m = m_new;
-    sm.pm[w][lane] = pw;
-    if (g == 0) sm.alpha[n][w] = alpha;
+    sm.pm[cur][w][lane] = pw;
+    if (g == 0) sm.alpha[cur][n][w] = alpha;
   }
   lds_barrier();
-
-  // ---- 3. rescale and accumulate O^T += V^T . P^T for all four row blocks
-  uint4 pb[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) pb[rb] = sm.pm[rb][lane];
-  const float4 al = *(const float4*)&sm.alpha[n][0];
-  const float alr[4] = {al.x, al.y, al.z, al.w};
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-    if (__builtin_amdgcn_ballot_w64(alr[rb] != 1.f) != 0) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) A.o[rb][e] *= alr[rb];
-    }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    // 16-bit element e of each staged chunk, two tokens per dword
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t a[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = (e >> 1) ? vt[2 * q].y : vt[2 * q].x;
-      const uint32_t hi = (e >> 1) ? vt[2 * q + 1].y : vt[2 * q + 1].x;
-      a[q] = __builtin_amdgcn_perm(hi, lo, sel);
-    }
-    const uint4 av = make_uint4(a[0], a[1], a[2], a[3]);
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) A.o[rb][e] = mfma_k32<QT>(av, pb[rb], A.o[rb][e]);
-  }
 }
 
 // A run: tiles [begin, end) whose pages (at most 64, from pg_begin) have
@@ -319,6 +331,7 @@ __device__ __forceinline__ Run open_run(const Params& p, const Piece& P, int run
 template <int QT, int NS>
 __device__ __forceinline__ void stream_piece(const Params& p, const Piece& P, const QRegs& Q, Run R,
                                              int t_to, Smem& sm, Acc& A) {
+  const int t_first = R.begin;
   while (true) {
     KTile buf[NS];
 #pragma unroll
@@ -331,12 +344,14 @@ __device__ __forceinline__ void stream_piece(const Params& p, const Piece& P, co
       for (int k = 0; k < NS; ++k) {
         const int tl = t + k + NS - 1;
         load_tile(p, P, R.my_page, R.pg_begin, tl < R.end, tl, buf[(k + NS - 1) % NS]);
-        if (k == 0 || t + k < R.end) compute_tile<QT>(p, P, Q, buf[k], t + k, sm, A);
+        if (k == 0 || t + k < R.end) compute_tile<QT>(p, P, Q, buf[k], t + k, t + k > t_first, sm, A);
       }
     }
     if (R.end >= t_to) break;
     R = open_run(p, P, R.end, t_to);
   }
+  // drain: the last tile's P . V (its P is visible after the last barrier)
+  if (t_to > t_first) pv_tile<QT>((t_to - 1) & 1, sm, A);
 }
 
 __device__ __forceinline__ void reset(Acc& A) {
