@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 typedef enum {
   PKV_OK = 0,
@@ -128,6 +128,13 @@ typedef struct pkv_options {
                              the call's stream after the split-KV kernel and
                              before the combine kernel (timing one kernel with
                              events; no work changes)                       */
+  /* xqa page, parameters `q_scale` / `kv_scale`: each may be a tensor.  When
+   * set, these point at one fp32 value in device memory, 4-byte aligned and
+   * caller-owned, and replace the q_scale / kv_scale arguments of the call.
+   * The kernels read them when they run (a captured graph replays with the
+   * values current at replay time); they must be finite. */
+  const float* q_scale_dev;
+  const float* kv_scale_dev;
 } pkv_options;
 
 /* The plan a decode call would use (pkv_query_plan). */

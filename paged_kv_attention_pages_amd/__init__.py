@@ -52,7 +52,8 @@ class Dims(ctypes.Structure):
 class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("split_pages", ctypes.c_int32),
                 ("num_cus", ctypes.c_int32), ("target_ctas", ctypes.c_int32),
-                ("split_event", ctypes.c_void_p)]
+                ("split_event", ctypes.c_void_p), ("q_scale_dev", ctypes.c_void_p),
+                ("kv_scale_dev", ctypes.c_void_p)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -131,14 +132,27 @@ def _dims(q, k_cache, page_table, head_dim_v, q_seq_len, workspace_bytes=0) -> D
     return d
 
 
-def _options(path=None, split_pages=0, num_cus=0, target_ctas=0, split_event=None):
-    if not (path or split_pages or num_cus or target_ctas or split_event):
+def _options(path=None, split_pages=0, num_cus=0, target_ctas=0, split_event=None,
+             q_scale_dev=None, kv_scale_dev=None):
+    if not (path or split_pages or num_cus or target_ctas or split_event or q_scale_dev
+            or kv_scale_dev):
         return None
     o = Options()
     o.path = {None: 0, "auto": 0, "valu": 1, "mfma": 2, "mfma_mla": 3}.get(path, path)
     o.split_pages, o.num_cus, o.target_ctas = split_pages, num_cus, target_ctas
     o.split_event = split_event
+    o.q_scale_dev, o.kv_scale_dev = q_scale_dev, kv_scale_dev
     return o
+
+
+def _scale_arg(x, name, device):
+    """A scale given as a float, or (as the xqa page allows) a one-element fp32
+    device tensor: returns (host value, device pointer or None)."""
+    if isinstance(x, torch.Tensor):
+        if (x.dtype != torch.float32 or x.numel() != 1 or x.device != device):
+            raise PkvError(1, f"{name} tensor must hold one float32 on {device}")
+        return 1.0, x.data_ptr()
+    return float(x), None
 
 
 def query_plan(*, batch, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, pages_per_seq,
@@ -225,9 +239,11 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
     forms); caches NHD [P, page_size, Hkv, D] or HND [P, Hkv, page_size, D]
     in q's dtype or float8_e4m3fn (uint8 bytes are read as e4m3fn); pass the
     same tensor as k_cache and v_cache with head_dim_v < Dqk for a latent
-    (MLA) cache whose rows start with V.  ``split_event`` (a torch.cuda.Event
-    that has been recorded once) is recorded between the split-KV and the
-    combine kernel.  Returns ``output``.
+    (MLA) cache whose rows start with V.  ``q_scale`` / ``kv_scale`` are
+    floats or one-element float32 device tensors (read by the kernels when
+    they run).  ``split_event`` (a torch.cuda.Event that has been recorded
+    once) is recorded between the split-KV and the combine kernel.  Returns
+    ``output``.
     """
     if head_dim_v is None:
         head_dim_v = output.shape[-1]
@@ -240,7 +256,9 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
             raise PkvError(1, "sinks must be contiguous float32 [num_kv_heads, head_group_ratio]")
     L = lib()
     ev = None if split_event is None else split_event.cuda_event
-    opts = _options(path, split_pages, 0, target_ctas, ev)
+    q_scale, q_scale_dev = _scale_arg(q_scale, "q_scale", q.device)
+    kv_scale, kv_scale_dev = _scale_arg(kv_scale, "kv_scale", q.device)
+    opts = _options(path, split_pages, 0, target_ctas, ev, q_scale_dev, kv_scale_dev)
     d = _dims(q, k_cache, page_table, head_dim_v, q_seq_len)
     if workspace_buffer is None:
         info = PlanInfo()

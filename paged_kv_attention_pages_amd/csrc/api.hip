@@ -224,6 +224,8 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
     return fail(PKV_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache and out must be 16-byte aligned");
   if (!std::isfinite(q_scale) || !std::isfinite(kv_scale))
     return fail(PKV_ERR_INVALID_ARGUMENT, "q_scale and kv_scale must be finite");
+  if (opts && (misaligned(opts->q_scale_dev, 4) || misaligned(opts->kv_scale_dev, 4)))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "device q_scale / kv_scale must be 4-byte aligned");
   if (pl.ws_bytes > 0) {
     if (workspace == nullptr)
       return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "workspace is NULL; %zu bytes needed", pl.ws_bytes);
@@ -274,6 +276,11 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
   p.qk_scale_log2 = (float)((double)q_scale * (double)kv_scale / std::sqrt((double)Dk) *
                             1.4426950408889634);
   p.out_scale = kv_scale;
+  p.q_scale_dev = opts ? opts->q_scale_dev : nullptr;
+  p.kv_scale_dev = opts ? opts->kv_scale_dev : nullptr;
+  p.q_scale = q_scale;
+  p.kv_scale = kv_scale;
+  p.qk_unit = (float)(1.4426950408889634 / std::sqrt((double)Dk));
   if (p.B > 65535 || Hkv > 65535)
     return fail(PKV_ERR_UNSUPPORTED, "batch and num_kv_heads must be <= 65535");
 

@@ -22,6 +22,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // grid (rows, Hkv, B), one wave per row; lane handles 4 consecutive dims
 template <int QT>
 __global__ __launch_bounds__(64) void combine_kernel(Params p) {
+  resolve_scales(p);
   const int r = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const SeqGeom sg = seq_geom(p, b);
   if (sg.nsplits == 1) return;
@@ -68,6 +69,7 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
 // readlane and eight slots' partial outputs are loaded at a time.
 template <int QT>
 __global__ __launch_bounds__(256) void combine_sk_kernel(Params p) {
+  resolve_scales(p);
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.z * 4 + (threadIdx.x >> 6);

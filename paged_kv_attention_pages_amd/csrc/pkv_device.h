@@ -35,7 +35,23 @@ struct Params {
   int sk_shift;               // stream-K tiles are 1 << sk_shift tokens
   float qk_scale_log2;        // q_scale * kv_scale / sqrt(Dqk) * log2(e)
   float out_scale;            // kv_scale (V dequantisation, applied once)
+  // device-resident scales (null: the host values above hold)
+  const float* q_scale_dev;
+  const float* kv_scale_dev;
+  float q_scale, kv_scale;    // host values, for a kernel that reads one scale
+  float qk_unit;              // Dqk^-1/2 * log2(e)
 };
+
+// Scales from device memory when the call passed them there: every kernel
+// calls this first, so all of them see the same values.
+__device__ __forceinline__ void resolve_scales(Params& p) {
+  if (p.q_scale_dev != nullptr || p.kv_scale_dev != nullptr) {
+    const float qs = p.q_scale_dev != nullptr ? *p.q_scale_dev : p.q_scale;
+    const float ks = p.kv_scale_dev != nullptr ? *p.kv_scale_dev : p.kv_scale;
+    p.qk_scale_log2 = qs * ks * p.qk_unit;
+    p.out_scale = ks;
+  }
+}
 
 // Token range of sequence b that any of its query rows can see, and the
 // split-KV chunking of the pages that hold it.  Shared by the split and the

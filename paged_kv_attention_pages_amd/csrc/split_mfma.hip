@@ -308,6 +308,7 @@ __device__ __forceinline__ void reset(Acc<D>& A) {
 // `split_pages` pages of the sequence's visible span.
 template <int QT, int KT, int D>
 __global__ __launch_bounds__(64) void split_mfma16_kernel(Params p) {
+  resolve_scales(p);
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const SeqGeom sg = seq_geom(p, b);
   if (split >= sg.nsplits) return;
@@ -331,6 +332,7 @@ template <int QT, int KT, int D>
 // (two waves per SIMD: the register budget keeps the accumulators in
 // architected VGPRs instead of moving them through AGPRs every tile)
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma16_sk_kernel(Params p) {
+  resolve_scales(p);
   const SkSched S = sk_schedule(p);
   const int w = blockIdx.x, W = sk_waves_eff(S.T, gridDim.x);
   if (w >= W) return;

@@ -386,6 +386,7 @@ __device__ __forceinline__ void finish_piece(const Params& p, const Piece& P, Ac
 // Grid schedule: one workgroup per (split, KV head, sequence).
 template <int QT>
 __global__ __launch_bounds__(kThreads) void split_mla_kernel(Params p) {
+  resolve_scales(p);
   __shared__ Smem sm;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const SeqGeom sg = seq_geom(p, b);
@@ -412,6 +413,7 @@ __global__ __launch_bounds__(kThreads) void split_mla_kernel(Params p) {
 // workspace slots 2w and 2w+1.
 template <int QT>
 __global__ __launch_bounds__(kThreads) void split_mla_sk_kernel(Params p) {
+  resolve_scales(p);
   __shared__ Smem sm;
   // the schedule's per-sequence tile prefix sums and counts live in LDS, so
   // the unit loop carries no per-lane schedule state

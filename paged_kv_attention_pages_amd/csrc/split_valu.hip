@@ -118,6 +118,7 @@ __device__ __forceinline__ uint4 to16x8(const uint4& raw) {
 
 template <int QT, int KT, int NR>
 __global__ __launch_bounds__(256) void split_valu_kernel(Params p) {
+  resolve_scales(p);
   constexpr int D = 128;
   __shared__ float s_acc[4][NR][D];
   __shared__ float s_m[4][NR], s_l[4][NR];

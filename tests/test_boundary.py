@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (pkv_\w+)", out))
     assert set(names) <= exported, set(names) - exported
-    assert pkv.lib().pkv_abi_version() == 1
+    assert pkv.lib().pkv_abi_version() == 2
 
 
 def test_struct_layouts_match_header(tmp_path):
@@ -52,7 +52,7 @@ int main(void) {
   printf("pkv_dims %zu\\n", sizeof(pkv_dims));
   printf("pkv_options %zu\\n", sizeof(pkv_options));
   printf("pkv_plan_info %zu\\n", sizeof(pkv_plan_info));
-  F(pkv_dims, workspace_bytes) F(pkv_dims, kv_dtype) F(pkv_options, target_ctas) F(pkv_options, split_event)
+  F(pkv_dims, workspace_bytes) F(pkv_dims, kv_dtype) F(pkv_options, target_ctas) F(pkv_options, split_event) F(pkv_options, q_scale_dev) F(pkv_options, kv_scale_dev)
   F(pkv_plan_info, workspace_bytes) F(pkv_plan_info, num_cus)
   return 0;
 }
@@ -69,6 +69,8 @@ int main(void) {
     assert int(got["pkv_dims.kv_dtype"]) == pkv.Dims.kv_dtype.offset
     assert int(got["pkv_options.target_ctas"]) == pkv.Options.target_ctas.offset
     assert int(got["pkv_options.split_event"]) == pkv.Options.split_event.offset
+    assert int(got["pkv_options.q_scale_dev"]) == pkv.Options.q_scale_dev.offset
+    assert int(got["pkv_options.kv_scale_dev"]) == pkv.Options.kv_scale_dev.offset
     assert int(got["pkv_plan_info.workspace_bytes"]) == pkv.PlanInfo.workspace_bytes.offset
     assert int(got["pkv_plan_info.num_cus"]) == pkv.PlanInfo.num_cus.offset
 

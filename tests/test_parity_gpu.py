@@ -564,3 +564,64 @@ def test_graph_replay_matches_eager(name):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {r} differs from the eager call"
+
+
+@pytest.mark.parametrize("name", ["gqa", "fp8", "mla"])
+def test_device_resident_scales(name):
+    # the xqa page's q_scale / kv_scale may be tensors: one fp32 value in
+    # device memory, read when the kernels run
+    base = {"gqa": SMALL["gqa"], "fp8": SMALL["fp8"], "mla": MLA_SMALL}[name]
+    w = base.replace(q_scale=0.7, kv_scale=base.kv_scale * 1.3)
+    print(f"[case] device scales {name}", flush=True)
+    inp = make(w, seed=100)
+    ref = run_oracle(w, inp)
+    qs = torch.tensor([w.q_scale], dtype=torch.float32, device=DEV)
+    ks = torch.tensor([w.kv_scale], dtype=torch.float32, device=DEV)
+    out = torch.full((w.batch, w.q_seq_len, w.num_q_heads, w.head_dim_v), float("nan"),
+                     dtype=w.q_dtype, device=DEV)
+    for split in (0, 1):
+        pkv.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"],
+                        inp["seq_lens"], out, num_kv_heads=w.num_kv_heads, page_size=w.page_size,
+                        sinks=inp["sinks"], q_scale=qs, kv_scale=ks, sliding_win_size=w.window,
+                        kv_layout=w.kv_layout, q_seq_len=w.q_seq_len, mask=inp["mask"],
+                        head_dim_v=w.head_dim_v, split_pages=split)
+        torch.cuda.synchronize()
+        assert_parity(w, out, ref, f"dev-scales/{name}/split{split}")
+    # a captured call picks up new values at replay
+    w2 = w.replace(q_scale=1.1, kv_scale=w.kv_scale * 0.8)
+    ref2 = run_oracle(w2, inp)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    plan = pkv.query_plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                          head_dim_qk=w.head_dim_qk, head_dim_v=w.head_dim_v,
+                          pages_per_seq=inp["page_table"].shape[1], page_size=w.page_size,
+                          q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, window=w.window,
+                          q_seq_len=w.q_seq_len)
+    ws = torch.empty(max(plan["workspace_bytes"], 256), dtype=torch.uint8, device=DEV)
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            pkv.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"],
+                            inp["seq_lens"], out, ws, num_kv_heads=w.num_kv_heads,
+                            page_size=w.page_size, sinks=inp["sinks"], q_scale=qs, kv_scale=ks,
+                            sliding_win_size=w.window, kv_layout=w.kv_layout,
+                            q_seq_len=w.q_seq_len, mask=inp["mask"], head_dim_v=w.head_dim_v)
+    torch.cuda.current_stream().wait_stream(s)
+    qs.fill_(w2.q_scale)
+    ks.fill_(w2.kv_scale)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert_parity(w2, out, ref2, f"dev-scales-replay/{name}")
+
+
+def test_device_scale_arguments_checked():
+    w = SMALL["gqa"]
+    inp = make(w, seed=101)
+    out = torch.empty((w.batch, 1, w.num_q_heads, 128), dtype=w.q_dtype, device=DEV)
+    for bad in (torch.ones(2, device=DEV), torch.ones(1, dtype=torch.float16, device=DEV),
+                torch.ones(1)):
+        with pytest.raises(pkv.PkvError, match="q_scale tensor"):
+            pkv.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"],
+                            inp["seq_lens"], out, num_kv_heads=w.num_kv_heads,
+                            page_size=w.page_size, kv_layout=w.kv_layout, q_scale=bad)
