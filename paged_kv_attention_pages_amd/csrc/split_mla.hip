@@ -170,16 +170,30 @@ __device__ __forceinline__ void score_tile(const Params& p, const Piece& P, cons
                                            int slot, Smem& sm, f32x4 (&s4)[2]) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4, w = wave_id();
   const int h = w >> 2;
-  const uint8_t* tl = sm.tile[slot];
-  // ---- 1. partial scores over dims [288 h, 288 h + 288)
+  // ---- 1. partial scores over dims [288 h, 288 h + 288): the 18 K
+  // fragments (two 16-token blocks x nine steps) are read kAhead ahead of
+  // their MFMA, so LDS latency overlaps the matrix work
+  const uint8_t* r = sm.tile[slot] + n * kPitch + 2 * kQkHalf * h + 16 * g;
+  constexpr int kFrags = 2 * kQkSteps, kAhead = 4;
+  auto frag = [&](int j) { return *(const uint4*)(r + (j / kQkSteps) * 16 * kPitch + 64 * (j % kQkSteps)); };
+  uint4 kf[kAhead];
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    const uint8_t* r = tl + (16 * tb + n) * kPitch + 2 * kQkHalf * h + 16 * g;
-    f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kAhead; ++j) kf[j] = frag(j);
+  s4[0] = s4[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < kQkSteps; ++s) a = mfma_k32<QT>(*(const uint4*)(r + 64 * s), Q.k[s], a);
-    s4[tb] = a;
+  for (int j = 0; j < kFrags; ++j) {
+    const uint4 cur = kf[j % kAhead];
+    if (j + kAhead < kFrags) kf[j % kAhead] = frag(j + kAhead);
+    s4[j / kQkSteps] = mfma_k32<QT>(cur, Q.k[j % kQkSteps], s4[j / kQkSteps]);
   }
+  // keep the order: kAhead reads, then (MFMA, read) pairs, then the last MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+  for (int j = 0; j < kFrags - kAhead; ++j) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
 }
 
 template <int QT>
@@ -310,10 +324,11 @@ __device__ __forceinline__ void stream_piece(const Params& p, const Piece& P, co
 #pragma unroll
       for (int k = 0; k < kLoadRing; ++k) {
         const int tt = t + k;
-        if (k == 0 || tt < te) {
-          const int i = tt - tb0;
-          const int slot = i % kRing, par = i & 1;
-          f32x4 s4[2];
+        const bool act = k == 0 || tt < te;
+        const int i = tt - tb0;
+        const int slot = i % kRing, par = i & 1;
+        f32x4 s4[2];
+        if (act) {
           score_tile<QT>(p, P, Q, tt, slot, sm, s4);
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) sm.sp[par][rb][h][tb][lane] = s4[tb];
@@ -321,9 +336,11 @@ __device__ __forceinline__ void stream_piece(const Params& p, const Piece& P, co
           // tile tt + 2 into the slot tile tt - 1 used (every wave finished
           // tile tt - 1 before it reached this step's barrier)
           store_tile(lr[k], (i + 2) % kRing, sm);
-          load_tile(p, P, R.my_page, R.pg_begin, tt + 2 + kLoadRing < te, tt + 2 + kLoadRing, lr[k]);
-          finish_tile<QT>(p, P, tt, slot, par, s4, sm, A);
         }
+        // issued on every step, live or not, so the wait counts before the
+        // stores stay exact and kLoadRing tiles remain in flight
+        load_tile(p, P, R.my_page, R.pg_begin, tt + 2 + kLoadRing < te, tt + 2 + kLoadRing, lr[k]);
+        if (act) finish_tile<QT>(p, P, tt, slot, par, s4, sm, A);
       }
     }
     if (te >= t_to) break;
