@@ -45,15 +45,23 @@ constexpr int kQkSteps = kQkHalf / 32;        // 9 MFMA K steps
 constexpr int kPvHalf = kDv / 2;              // 256 output dims per half
 constexpr int kTileTok = 32;                  // tokens per tile
 constexpr int kTileShift = 5;
-constexpr int kRowBytes = kDqk * 2;           // 1152
-constexpr int kPitch = kRowBytes + 16;        // LDS row pitch: 16 B skew per row
-constexpr int kTileBytes = kTileTok * kPitch;
+// LDS tile: two halves of 16 rows; a half holds the first 1024 bytes of its
+// rows (dims 0 .. 511) at 1024 bytes per row, then the last 128 bytes (the
+// rope dims) at 128 bytes per row.  The 16-byte chunks of a row are
+// XOR-swizzled (swz_lo / swz_hi) so that the K reads (sixteen rows, one
+// chunk), the transposed V reads (eight rows, 32 bytes each) and the row
+// stores each hit distinct banks.
+constexpr int kLoBytes = 1024, kHiBytes = 128;
+constexpr int kHiOff = 16 * kLoBytes;         // rope part of a half
+constexpr int kHalfBytes = 16 * (kLoBytes + kHiBytes);
+constexpr int kTileBytes = 2 * kHalfBytes;
 constexpr int kRing = 3;                      // LDS tiles in flight
 constexpr int kLoadRing = 3;                  // register tiles in flight per wave
+static_assert(kLoadRing == kRing, "the step loop indexes the LDS ring by its unroll index");
 static_assert(kQkHalf % 32 == 0 && kPvHalf % 64 == 0, "latent row split");
 
 struct Smem {
-  uint8_t tile[kRing][kTileBytes];           // 32 rows of the cache, pitch kPitch
+  uint8_t tile[kRing][kTileBytes];           // 32 rows of the cache, layout above
   f32x4 sp[2][4][2][2][64];                  // partial scores [parity][row block][half][token block]
 };
 
@@ -82,8 +90,14 @@ struct Piece {
 };
 
 struct Acc {
-  f32x4 o[4][4];   // [64-dim group q][e]: dims 256 h + 64 q + 4 (4 g + i) + e, row 16 rb + n
+  f32x4 o[16];     // [m][i]: dims 256 h + 16 m + 4 g + i, row 16 rb + n
   float m, l;      // running reference max (log2 units) and this lane's part of the sum
+};
+
+// Per-lane LDS byte offsets inside a tile slot, fixed for the kernel.
+struct LdsOff {
+  int k[9];   // K fragment of step s, half 0 (half 1: + kHalfBytes)
+  int v[8];   // transposed V read of MFMA m (k = m mod 8; + 256 (m / 8)), half 0
 };
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -95,6 +109,47 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Chunk swizzles of row r (0 .. 15) of a half tile: chunk c of the low part
+// sits at c ^ swz_lo(r) (within its aligned group of 16), chunk c of the rope
+// part at c ^ swz_hi(r).
+__device__ __forceinline__ int swz_lo(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_hi(int r) { return (r >> 1) & 7; }
+// byte offset of 16-byte chunk c of a row's low part, chunk-swizzled
+__device__ __forceinline__ int lo_chunk(int r, int c) { return r * kLoBytes + 16 * ((c & ~15) | ((c & 15) ^ swz_lo(r))); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposed LDS read (ds_read_b64_tr_b16).  In each group of 16 lanes, lane
+// a + 4 j supplies the address of four 16-bit elements; lane 4 a + e
+// receives element e of lanes a, a + 4, a + 8, a + 12, in that order.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint8_t* addr) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(addr));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Score step s reads chunk c = 36 h + 4 s + g of row n of each half: with
+// s = j + 4 i that is chunk (36 h + g + 4 j) + 16 i of the low part (the
+// swizzle leaves the + 16 i alone), except steps 7 and 8 of half 1, which
+// are the rope chunks g and 4 + g.  V read m of lane (n, g) covers row
+// 4 g + n / 4 of each half, chunk 32 h + 2 m + (n / 2 mod 2), byte 8 (n mod 2).
+__device__ __forceinline__ LdsOff lds_offsets() {
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4, h = wave_id() >> 2;
+  LdsOff o;
+  const int c0 = 36 * h + g;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o.k[j] = lo_chunk(n, c0 + 4 * j);
+#pragma unroll
+  for (int s = 4; s < 7; ++s) o.k[s] = o.k[s & 3] + 256 * (s >> 2);
+  const int hi = kHiOff + n * kHiBytes;
+  o.k[7] = h ? hi + 16 * (g ^ swz_hi(n)) : o.k[3] + 256;
+  o.k[8] = h ? hi + 16 * ((4 + g) ^ swz_hi(n)) : o.k[0] + 512;
+  const int r = 4 * g + (n >> 2), bsel = (n >> 1) & 1;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o.v[k] = lo_chunk(r, 32 * h + 2 * k + bsel) + 8 * (n & 1);
+  return o;
 }
 
 __device__ __forceinline__ void setup_piece(const Params& p, int b, int kvh, int tok_lo, int tok_hi,
@@ -157,25 +212,26 @@ __device__ __forceinline__ void load_tile(const Params& p, const Piece& P, int m
 // Write this wave's rows of a tile into LDS ring slot `slot`.
 __device__ __forceinline__ void store_tile(const LTile& T, int slot, Smem& sm) {
   const int lane = threadIdx.x & 63, n = lane & 15, w = wave_id();
-  uint8_t* row = sm.tile[slot] + (4 * w + (lane >> 4)) * kPitch;
+  const int r = 4 * (w & 3) + (lane >> 4);   // row in half tile w / 4
+  uint8_t* half = sm.tile[slot] + (w >> 2) * kHalfBytes;
+  // chunk n + 16 j lands at 16 j + (n ^ swz_lo(r))
+  uint8_t* lo = half + lo_chunk(r, n);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) *(uint4*)(row + 16 * n + 256 * j) = T.a[j];
-  *(uint2*)(row + 1024 + 8 * n) = T.b;
+  for (int j = 0; j < 4; ++j) *(uint4*)(lo + 256 * j) = T.a[j];
+  *(uint2*)(half + kHiOff + r * kHiBytes + 16 * ((n >> 1) ^ swz_hi(r)) + 8 * (n & 1)) = T.b;
 }
 
 // One tile from LDS ring slot `slot`: partial scores, swap, softmax, P . V.
 // `par` selects the partial-score buffer (tile parity).
 template <int QT>
-__device__ __forceinline__ void score_tile(const Params& p, const Piece& P, const QRegs& Q, int t,
-                                           int slot, Smem& sm, f32x4 (&s4)[2]) {
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4, w = wave_id();
-  const int h = w >> 2;
+__device__ __forceinline__ void score_tile(const Params& p, const Piece& P, const QRegs& Q, const LdsOff& L,
+                                           int t, int slot, Smem& sm, f32x4 (&s4)[2]) {
   // ---- 1. partial scores over dims [288 h, 288 h + 288): the 18 K
   // fragments (two 16-token blocks x nine steps) are read kAhead ahead of
   // their MFMA, so LDS latency overlaps the matrix work
-  const uint8_t* r = sm.tile[slot] + n * kPitch + 2 * kQkHalf * h + 16 * g;
+  const uint8_t* tl = sm.tile[slot];
   constexpr int kFrags = 2 * kQkSteps, kAhead = 4;
-  auto frag = [&](int j) { return *(const uint4*)(r + (j / kQkSteps) * 16 * kPitch + 64 * (j % kQkSteps)); };
+  auto frag = [&](int j) { return *(const uint4*)(tl + (j / kQkSteps) * kHalfBytes + L.k[j % kQkSteps]); };
   uint4 kf[kAhead];
 #pragma unroll
   for (int j = 0; j < kAhead; ++j) kf[j] = frag(j);
@@ -197,15 +253,26 @@ __device__ __forceinline__ void score_tile(const Params& p, const Piece& P, cons
 }
 
 template <int QT>
-__device__ __forceinline__ void finish_tile(const Params& p, const Piece& P, int t, int slot, int par,
-                                            const f32x4 (&s4)[2], Smem& sm, Acc& A) {
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4, w = wave_id();
+__device__ __forceinline__ void finish_tile(const Params& p, const Piece& P, const LdsOff& L, int t, int slot,
+                                            int par, const f32x4 (&s4)[2], Smem& sm, Acc& A) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, w = wave_id();
   const int rb = w & 3, h = w >> 2;
   const int tok0 = t * kTileTok;
   // ---- 2. the other half's partials (the sum a + b is the same bits on both sides)
   f32x4 sc[2];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) sc[tb] = s4[tb] + sm.sp[par][rb][h ^ 1][tb][lane];
+  // the first V^T operands (step 3) are read now, under the softmax
+  const uint8_t* tl = sm.tile[slot];
+  auto vread = [&](int m) {
+    const int o = L.v[m & 7] + 256 * (m >> 3);
+    const uint2 v0 = lds_read_tr16(tl + o), v1 = lds_read_tr16(tl + kHalfBytes + o);
+    return make_uint4(v0.x, v0.y, v1.x, v1.y);
+  };
+  constexpr int kVAhead = 3;
+  uint4 vf[kVAhead];
+#pragma unroll
+  for (int j = 0; j < kVAhead; ++j) vf[j] = vread(j);
   float x[2][4];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
@@ -247,35 +314,26 @@ __device__ __forceinline__ void finish_tile(const Params& p, const Piece& P, int
   A.m = m_new;
   if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) A.o[q][e] *= alpha;
+    for (int m = 0; m < 16; ++m) A.o[m] *= alpha;
   }
-  // ---- 3. O^T += V^T . P^T over dims [256 h, 256 h + 256), 64 at a time:
-  // lane (n, g) reads dims 4 n .. 4 n + 4 of the eight tokens of its K block
-  const uint8_t* tl = sm.tile[slot];
+  // ---- 3. O^T += V^T . P^T over dims [256 h, 256 h + 256), 16 (MFMA m) at
+  // a time.  The V^T operand comes from two transposed reads, one per half
+  // tile: lane a + 4 j of group g supplies dims 16 m + 4 a .. + 4 of token
+  // 16 hh + 4 g + j, so lane n of group g receives dim 16 m + n of tokens
+  // 16 hh + 4 g + (0 .. 3) -- MFMA K index 8 g + 4 hh + j, as in P^T.
+  // Reads run kVAhead MFMAs ahead.
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint2 vt[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int tk = c < 4 ? 4 * g + c : 16 + 4 * g + (c - 4);
-      vt[c] = *(const uint2*)(tl + tk * kPitch + 2 * (kPvHalf * h + 64 * q + 4 * n));
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // 16-bit element e of each 8-byte chunk, two tokens per dword
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t a[4];
-#pragma unroll
-      for (int c2 = 0; c2 < 4; ++c2) {
-        const uint32_t lo = (e >> 1) ? vt[2 * c2].y : vt[2 * c2].x;
-        const uint32_t hi = (e >> 1) ? vt[2 * c2 + 1].y : vt[2 * c2 + 1].x;
-        a[c2] = __builtin_amdgcn_perm(hi, lo, sel);
-      }
-      A.o[q][e] = mfma_k32<QT>(make_uint4(a[0], a[1], a[2], a[3]), pw, A.o[q][e]);
-    }
+  for (int m = 0; m < 16; ++m) {
+    const uint4 cur = vf[m % kVAhead];
+    if (m + kVAhead < 16) vf[m % kVAhead] = vread(m + kVAhead);
+    A.o[m] = mfma_k32<QT>(cur, pw, A.o[m]);
   }
+#pragma unroll
+  for (int m = 0; m + kVAhead < 16; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kVAhead, 0);
 }
 
 // A run: tiles [begin, end) whose pages (at most 64, from pg_begin) have
@@ -302,7 +360,7 @@ __device__ __forceinline__ Run open_run(const Params& p, const Piece& P, int run
 // finishes tile t.  The register ring holds kLoadRing tiles in flight per
 // wave; the loop is unrolled by kLoadRing to index it statically.
 template <int QT>
-__device__ __forceinline__ void stream_piece(const Params& p, const Piece& P, const QRegs& Q, Run R,
+__device__ __forceinline__ void stream_piece(const Params& p, const Piece& P, const QRegs& Q, const LdsOff& L, Run R,
                                              int t_to, Smem& sm, Acc& A) {
   const int lane = threadIdx.x & 63, w = wave_id();
   const int rb = w & 3, h = w >> 2;
@@ -326,10 +384,10 @@ __device__ __forceinline__ void stream_piece(const Params& p, const Piece& P, co
         const int tt = t + k;
         const bool act = k == 0 || tt < te;
         const int i = tt - tb0;
-        const int slot = i % kRing, par = i & 1;
+        const int slot = k, par = i & 1;   // i mod kRing == k: runs start at slot 0
         f32x4 s4[2];
         if (act) {
-          score_tile<QT>(p, P, Q, tt, slot, sm, s4);
+          score_tile<QT>(p, P, Q, L, tt, slot, sm, s4);
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) sm.sp[par][rb][h][tb][lane] = s4[tb];
           lds_barrier();
@@ -340,7 +398,7 @@ __device__ __forceinline__ void stream_piece(const Params& p, const Piece& P, co
         // issued on every step, live or not, so the wait counts before the
         // stores stay exact and kLoadRing tiles remain in flight
         load_tile(p, P, R.my_page, R.pg_begin, tt + 2 + kLoadRing < te, tt + 2 + kLoadRing, lr[k]);
-        if (act) finish_tile<QT>(p, P, tt, slot, par, s4, sm, A);
+        if (act) finish_tile<QT>(p, P, L, tt, slot, par, s4, sm, A);
       }
     }
     if (te >= t_to) break;
@@ -352,9 +410,7 @@ __device__ __forceinline__ void reset(Acc& A) {
   A.m = kNegInf;
   A.l = 0.f;
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) A.o[q][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < 16; ++m) A.o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // Normalised output when this workgroup saw the whole unit, else the
@@ -366,7 +422,7 @@ __device__ __forceinline__ void finish_piece(const Params& p, const Piece& P, Ac
   const int row = 16 * (w & 3) + n, h = w >> 2;
   const float l = sum_across_rows(A.l);
   if (row >= p.R) return;
-  // lane (n, g) holds dims 256 h + 64 q + 16 g + 4 i + e of its row
+  // lane (n, g) holds dims 256 h + 16 m + 4 g + i of its row
   if (complete) {
     float num = 1.f, den = l;
     if (p.sinks != nullptr) {
@@ -376,24 +432,16 @@ __device__ __forceinline__ void finish_piece(const Params& p, const Piece& P, Ac
       den = l * num + exp2f(sk - Mf);
     }
     const float inv = den > 0.f ? p.out_scale * num / den : 0.f;
-    uint16_t* o = (uint16_t*)p.out + q_row_offset(p, P.b, P.kvh, row) * kDv + kPvHalf * h + 16 * g;
+    uint16_t* o = (uint16_t*)p.out + q_row_offset(p, P.b, P.kvh, row) * kDv + kPvHalf * h + 4 * g;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        *(uint4*)(o + 64 * q + 8 * hh) =
-            make_uint4(pack2<QT>(A.o[q][0][2 * hh] * inv, A.o[q][1][2 * hh] * inv),
-                       pack2<QT>(A.o[q][2][2 * hh] * inv, A.o[q][3][2 * hh] * inv),
-                       pack2<QT>(A.o[q][0][2 * hh + 1] * inv, A.o[q][1][2 * hh + 1] * inv),
-                       pack2<QT>(A.o[q][2][2 * hh + 1] * inv, A.o[q][3][2 * hh + 1] * inv));
+    for (int m = 0; m < 16; ++m)
+      *(uint2*)(o + 16 * m) = make_uint2(pack2<QT>(A.o[m][0] * inv, A.o[m][1] * inv),
+                                         pack2<QT>(A.o[m][2] * inv, A.o[m][3] * inv));
   } else {
-    float* o = p.ws_o + (prow0 + row) * kDv + kPvHalf * h + 16 * g;
+    float* o = p.ws_o + (prow0 + row) * kDv + kPvHalf * h + 4 * g;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *(float4*)(o + 64 * q + 4 * i) =
-            make_float4(A.o[q][0][i], A.o[q][1][i], A.o[q][2][i], A.o[q][3][i]);
+    for (int m = 0; m < 16; ++m)
+      *(float4*)(o + 16 * m) = make_float4(A.o[m][0], A.o[m][1], A.o[m][2], A.o[m][3]);
     if (h == 0 && g == 0) p.ws_ml[prow0 + row] = make_float2(A.m, l);
   }
 }
@@ -419,7 +467,8 @@ __global__ __launch_bounds__(kThreads) void split_mla_kernel(Params p) {
   load_q(p, P, Q);
   Acc A;
   reset(A);
-  stream_piece<QT>(p, P, Q, R, t_to, sm, A);
+  const LdsOff L = lds_offsets();
+  stream_piece<QT>(p, P, Q, L, R, t_to, sm, A);
   finish_piece<QT>(p, P, A, sg.nsplits == 1,
                    (((int64_t)b * p.Hkv + kvh) * p.max_splits + split) * p.R);
 }
@@ -454,6 +503,7 @@ __global__ __launch_bounds__(kThreads) void split_mla_sk_kernel(Params p) {
   // the host keeps the tile stream under 2^31 tiles for this kernel
   const int x0 = (int)sk_wave_start(T, wg, W), x1 = (int)sk_wave_start(T, wg + 1, W);
   const int Hkv = p.Hkv;
+  const LdsOff L = lds_offsets();
   for (int x = x0; x < x1;) {
     Piece P;
     QRegs Q;
@@ -479,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void split_mla_sk_kernel(Params p) {
     const Run R = open_run(p, P, t_from, t_to);
     load_q(p, P, Q);
     reset(A);
-    stream_piece<QT>(p, P, Q, R, t_to, sm, A);
+    stream_piece<QT>(p, P, Q, L, R, t_to, sm, A);
     const bool complete = x == ustart && seg_end == ustart + ntiles;
     const int slot = 2 * wg + (x == x0 ? 0 : 1);
     finish_piece<QT>(p, P, A, complete, (int64_t)slot * p.R);
