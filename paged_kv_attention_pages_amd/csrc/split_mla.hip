@@ -358,9 +358,9 @@ __device__ __forceinline__ Run open_run(const Params& p, const Piece& P, int run
 
 // Tiles [R.begin, t_to) of a piece, run by run.  Per run: the first two
 // tiles go to LDS before the loop; in step t the workgroup scores tile t,
-// swaps partials (the one barrier), writes tile t + 2 into the ring slot
-// freed by tile t - 1, issues the loads of tile t + 2 + kLoadRing, and
-// finishes tile t.  The register ring holds kLoadRing tiles in flight per
+// swaps partials (the one barrier), finishes tile t, writes tile t + 2 into
+// the ring slot freed by tile t - 1 and issues the loads of tile
+// t + 2 + kLoadRing.  The register ring holds kLoadRing tiles in flight per
 // wave; the loop is unrolled by kLoadRing to index it statically.
 template <int QT>
 __device__ __forceinline__ void stream_piece(const Params& p, const Piece& P, const QRegs& Q, const LdsOff& L, Run R,
@@ -394,14 +394,16 @@ __device__ __forceinline__ void stream_piece(const Params& p, const Piece& P, co
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) sm.sp[par][rb][h][tb][lane] = s4[tb];
           lds_barrier();
+          finish_tile<QT>(p, P, L, tt, slot, par, s4, sm, A);
           // tile tt + 2 into the slot tile tt - 1 used (every wave finished
-          // tile tt - 1 before it reached this step's barrier)
+          // tile tt - 1 before it reached this step's barrier); stored after
+          // this tile's work, so a late load stalls the wave only once the
+          // step's matrix work is done, and still ahead of the next barrier
           store_tile(lr[k], (i + 2) % kRing, sm);
         }
         // issued on every step, live or not, so the wait counts before the
         // stores stay exact and kLoadRing tiles remain in flight
         load_tile(p, P, R.my_page, R.pg_begin, tt + 2 + kLoadRing < te, tt + 2 + kLoadRing, lr[k]);
-        if (act) finish_tile<QT>(p, P, L, tt, slot, par, s4, sm, A);
       }
     }
     if (te >= t_to) break;
