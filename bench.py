@@ -197,6 +197,7 @@ def main():
             "kv_bytes_per_call": kv_bytes, "cache_replicas": n_rep,
             "path": pkv.PATH_NAMES.get(plan["path"], plan["path"]),
             "split_pages": plan["split_pages"], "max_splits": plan["max_splits"],
+            "single_launch": bool(plan["single_launch"]),
         },
         "roofline": {
             "kernel": "split-KV decode (" + pkv.PATH_NAMES.get(plan["path"], "?") + ")",

@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 
 typedef enum {
   PKV_OK = 0,
@@ -135,6 +135,13 @@ typedef struct pkv_options {
    * values current at replay time); they must be finite. */
   const float* q_scale_dev;
   const float* kv_scale_dev;
+  /* Where the matrix-core stream-K plan merges the partials of a
+   * (sequence, KV head) cut across waves: 0 = planner's choice (in the split
+   * kernel when every wave's share is short, where the second launch would
+   * dominate; else in a combine kernel), 1 = combine kernel (two launches),
+   * 2 = split kernel (one launch).  Other plans always use the combine
+   * kernel.  (ABI version 3.) */
+  int32_t merge_mode;
 } pkv_options;
 
 /* The plan a decode call would use (pkv_query_plan). */
@@ -146,6 +153,8 @@ typedef struct pkv_plan_info {
   int32_t ctas_per_split_grid; /* workgroups launched by the split kernel   */
   int32_t num_cus;
   uint64_t workspace_bytes;    /* bytes the call needs                      */
+  int32_t single_launch;       /* 1: the split kernel merges its partials
+                                  itself (no combine kernel); ABI 3         */
 } pkv_plan_info;
 
 /* ABI version (PKV_ABI_VERSION of the built library). */
@@ -164,7 +173,11 @@ pkv_status pkv_query_plan(const pkv_dims* dims, int num_kv_heads, int page_size,
 /* Workspace bytes a decode call with these arguments needs (0 on invalid
  * arguments; pkv_last_error() says why).  The workspace holds the split-KV
  * partial results (running max, running sum and unnormalised output per
- * split), the role of the xqa page's `workspace_buffer`. */
+ * split), the role of the xqa page's `workspace_buffer`, and -- for the
+ * matrix-core stream-K plan -- one 8-byte counter per (sequence, KV head),
+ * the role of its `semaphores`.  No initialisation is needed: a counter word
+ * tagged by another call counts as zero, and a call leaves its counts at
+ * zero.  Calls that share a workspace must not run concurrently. */
 size_t pkv_workspace_size(const pkv_dims* dims, int num_kv_heads, int page_size,
                           int window, int q_seq_len);
 
@@ -174,9 +187,11 @@ size_t pkv_workspace_size(const pkv_dims* dims, int num_kv_heads, int page_size,
  * `window` is sliding_win_size (0 = off).  `mask` is read only when
  * q_seq_len > 1.  `workspace` must hold dims->workspace_bytes >=
  * pkv_workspace_size(...) bytes and be 256-byte aligned.  The xqa page's
- * `semaphores`, `sm_count`, `enable_pdl` and `rcp_out_scale` have no
- * counterpart: the split-KV reduction is a second kernel, the CU count is
- * queried, and the output scale is 1. */
+ * `semaphores` live in the workspace: on the matrix-core stream-K plan the
+ * last wave to finish a piece of a (sequence, KV head) merges its partials
+ * in the same launch; the latent-cache and split-grid plans merge in a second
+ * kernel.  `sm_count`, `enable_pdl` and `rcp_out_scale` have no counterpart:
+ * the CU count is queried and the output scale is 1. */
 pkv_status pkv_decode_attn(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* page_table, const uint32_t* seq_lens,
                            void* out, void* workspace, int num_kv_heads,

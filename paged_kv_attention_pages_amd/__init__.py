@@ -53,14 +53,14 @@ class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("split_pages", ctypes.c_int32),
                 ("num_cus", ctypes.c_int32), ("target_ctas", ctypes.c_int32),
                 ("split_event", ctypes.c_void_p), ("q_scale_dev", ctypes.c_void_p),
-                ("kv_scale_dev", ctypes.c_void_p)]
+                ("kv_scale_dev", ctypes.c_void_p), ("merge_mode", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("split_pages", ctypes.c_int32),
                 ("max_splits", ctypes.c_int32), ("rows", ctypes.c_int32),
                 ("ctas_per_split_grid", ctypes.c_int32), ("num_cus", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_uint64)]
+                ("workspace_bytes", ctypes.c_uint64), ("single_launch", ctypes.c_int32)]
 
 
 _lib = None
@@ -133,15 +133,16 @@ def _dims(q, k_cache, page_table, head_dim_v, q_seq_len, workspace_bytes=0) -> D
 
 
 def _options(path=None, split_pages=0, num_cus=0, target_ctas=0, split_event=None,
-             q_scale_dev=None, kv_scale_dev=None):
+             q_scale_dev=None, kv_scale_dev=None, single_launch=None):
     if not (path or split_pages or num_cus or target_ctas or split_event or q_scale_dev
-            or kv_scale_dev):
+            or kv_scale_dev or single_launch is not None):
         return None
     o = Options()
     o.path = {None: 0, "auto": 0, "valu": 1, "mfma": 2, "mfma_mla": 3}.get(path, path)
     o.split_pages, o.num_cus, o.target_ctas = split_pages, num_cus, target_ctas
     o.split_event = split_event
     o.q_scale_dev, o.kv_scale_dev = q_scale_dev, kv_scale_dev
+    o.merge_mode = 0 if single_launch is None else 2 if single_launch else 1
     return o
 
 
@@ -157,12 +158,13 @@ def _scale_arg(x, name, device):
 
 def query_plan(*, batch, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, pages_per_seq,
                page_size, q_dtype=torch.bfloat16, kv_dtype=None, num_pages=1, window=0,
-               q_seq_len=1, path=None, split_pages=0, num_cus=0, target_ctas=0) -> dict:
+               q_seq_len=1, path=None, split_pages=0, num_cus=0, target_ctas=0,
+               single_launch=None) -> dict:
     """The plan the library would use (host only when num_cus > 0)."""
     d = Dims(batch, num_q_heads, head_dim_qk, head_dim_v, pages_per_seq, num_pages,
              _DTYPE[q_dtype], _DTYPE[kv_dtype or q_dtype], 0)
     info = PlanInfo()
-    o = _options(path, split_pages, num_cus, target_ctas)
+    o = _options(path, split_pages, num_cus, target_ctas, single_launch=single_launch)
     _check(lib().pkv_query_plan(ctypes.byref(d), num_kv_heads, page_size, window, q_seq_len,
                                 None if o is None else ctypes.byref(o), ctypes.byref(info)))
     return {f: getattr(info, f) for f, _ in PlanInfo._fields_}
@@ -232,7 +234,8 @@ def _shape_checks(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_head
 def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buffer=None, *,
                 num_kv_heads, page_size, sinks=None, q_scale=1.0, kv_scale=1.0,
                 sliding_win_size=0, kv_layout="NHD", q_seq_len=1, mask=None, head_dim_v=None,
-                path=None, split_pages=0, target_ctas=0, stream=None, split_event=None):
+                path=None, split_pages=0, target_ctas=0, stream=None, split_event=None,
+                single_launch=None):
     """Paged-KV decode attention, written in place into ``output``.
 
     q [B, q_seq_len, Hq, Dqk] (or [B, Hq, Dqk], or the xqa page's beam-1
@@ -242,8 +245,10 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
     (MLA) cache whose rows start with V.  ``q_scale`` / ``kv_scale`` are
     floats or one-element float32 device tensors (read by the kernels when
     they run).  ``split_event`` (a torch.cuda.Event that has been recorded
-    once) is recorded between the split-KV and the combine kernel.  Returns
-    ``output``.
+    once) is recorded after the split-KV kernel (before the combine kernel,
+    when the plan has one).  ``single_launch`` (None: the planner's choice)
+    makes the matrix-core stream-K plan merge cut units in the split kernel
+    (True) or in a second kernel (False).  Returns ``output``.
     """
     if head_dim_v is None:
         head_dim_v = output.shape[-1]
@@ -258,7 +263,8 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
     ev = None if split_event is None else split_event.cuda_event
     q_scale, q_scale_dev = _scale_arg(q_scale, "q_scale", q.device)
     kv_scale, kv_scale_dev = _scale_arg(kv_scale, "kv_scale", q.device)
-    opts = _options(path, split_pages, 0, target_ctas, ev, q_scale_dev, kv_scale_dev)
+    opts = _options(path, split_pages, 0, target_ctas, ev, q_scale_dev, kv_scale_dev,
+                    single_launch)
     d = _dims(q, k_cache, page_table, head_dim_v, q_seq_len)
     if workspace_buffer is None:
         info = PlanInfo()

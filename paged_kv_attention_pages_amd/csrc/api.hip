@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -61,8 +62,14 @@ struct Plan {
   int sk_waves;        // > 0: stream-K over this many persistent waves
   size_t ws_o_bytes;   // partial outputs
   size_t ws_ml_off;    // offset of (max, sum) pairs
+  size_t ws_cnt_off;   // offset of the per-unit counters (single-launch merge)
+  bool fused;          // cut units merged in the split kernel (no combine launch)
   size_t ws_bytes;
 };
+
+// Generation of a single-launch-merge call: tags the per-unit counters so
+// that words left by other calls count as zero.
+std::atomic<unsigned> g_gen{0};
 
 // Host-side checks shared by every entry point, then the plan.
 pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window, int Tq,
@@ -171,6 +178,8 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
   pl->max_splits = (int)S;
   pl->num_cus = cus;
   pl->sk_waves = 0;
+  pl->fused = false;
+  pl->ws_cnt_off = 0;
   // Stream-K schedule (matrix-core path, batch <= 256, no forced split size):
   // persistent waves (measured best: one per SIMD for 16-bit caches, each
   // with a three-stage pipeline in flight); 2 partial slots per wave.
@@ -192,6 +201,22 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
     pl->ws_o_bytes = nrow * Dv * sizeof(float);
     pl->ws_ml_off = (pl->ws_o_bytes + 255) & ~(size_t)255;
     pl->ws_bytes = pl->ws_ml_off + nrow * 2 * sizeof(float);
+    // The matrix-core kernel can merge cut units itself (one launch), with
+    // one 8-byte counter per unit after the partials.  The merge then sits
+    // at the end of the waves' shares, behind a few device-scope memory
+    // round trips; that beats a second launch only when the shares are
+    // short (measured, 64 sequences x 8 KV heads: 3 us per call gained at
+    // 16-128 tokens, even at 256, 1 us lost at 512 and more), so by default
+    // it is used when no wave's share can exceed 8 tiles.  The latent-cache
+    // kernel leaves the merge of its 64-row partials to the combine kernel.
+    const int mode = opts ? opts->merge_mode : 0;
+    const int64_t max_tiles = units * cdiv(pages_max * ps, 16);
+    pl->fused = path == PKV_PATH_MFMA &&
+                (mode == 2 || (mode == 0 && max_tiles <= 8 * (int64_t)pl->sk_waves));
+    if (pl->fused) {
+      pl->ws_cnt_off = (pl->ws_bytes + 255) & ~(size_t)255;
+      pl->ws_bytes = pl->ws_cnt_off + (size_t)units * sizeof(unsigned long long);
+    }
     return PKV_OK;
   }
   const size_t nrow = (size_t)d->batch * Hkv * S * R;
@@ -281,6 +306,9 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
   p.q_scale = q_scale;
   p.kv_scale = kv_scale;
   p.qk_unit = (float)(1.4426950408889634 / std::sqrt((double)Dk));
+  p.fused = pl.fused ? 1 : 0;
+  p.ws_cnt = pl.fused ? (unsigned long long*)((char*)workspace + pl.ws_cnt_off) : nullptr;
+  p.gen = pl.fused ? g_gen.fetch_add(1, std::memory_order_relaxed) + 1u : 0u;
   if (p.B > 65535 || Hkv > 65535)
     return fail(PKV_ERR_UNSUPPORTED, "batch and num_kv_heads must be <= 65535");
 
@@ -296,8 +324,10 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
     e = hipEventRecord((hipEvent_t)opts->split_event, s);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "event record failed: %s", hipGetErrorString(e));
   }
-  e = pkv::launch_combine(d->q_dtype, p, s);
-  if (e != hipSuccess) return fail(PKV_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
+  if (!pl.fused) {
+    e = pkv::launch_combine(d->q_dtype, p, s);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
+  }
   g_err.clear();
   return PKV_OK;
 }
@@ -327,6 +357,7 @@ pkv_status pkv_query_plan(const pkv_dims* dims, int num_kv_heads, int page_size,
       pl.sk_waves > 0 ? pl.sk_waves : pl.max_splits * num_kv_heads * dims->batch;
   info->num_cus = pl.num_cus;
   info->workspace_bytes = pl.ws_bytes;
+  info->single_launch = pl.fused ? 1 : 0;
   g_err.clear();
   return PKV_OK;
 }

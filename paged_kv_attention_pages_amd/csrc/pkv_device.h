@@ -40,6 +40,11 @@ struct Params {
   const float* kv_scale_dev;
   float q_scale, kv_scale;    // host values, for a kernel that reads one scale
   float qk_unit;              // Dqk^-1/2 * log2(e)
+  // single-launch merge (matrix-core stream-K): per-unit counters and the
+  // call's generation; fused == 0 leaves the merge to the combine kernel
+  unsigned long long* ws_cnt; // [B * Hkv]
+  unsigned gen;
+  int fused;
 };
 
 // Scales from device memory when the call passed them there: every kernel

@@ -294,6 +294,170 @@ __device__ __forceinline__ void finish_unit(const Params& p, const Unit<KT, D>& 
   }
 }
 
+// ---- single-launch merge of cut stream-K units
+//
+// The waves that share a cut unit each leave their partial (m, l, o) in the
+// workspace with device-scope stores, wait until those stores have
+// completed, and count on the unit's counter; the wave that brings the count
+// to the number of pieces merges all of them.  The stores and the merging
+// wave's loads are device-scope accesses (sc1: coherent across the XCDs'
+// L2 caches, as the compiler lowers agent-scope relaxed atomics), so no
+// cache write-back or invalidate is needed.  This is the role the xqa page
+// gives its `semaphores` buffer.
+//
+// Counter word of a unit: (call generation << 32) | pieces counted.  A word
+// from another call (another generation, or bytes another plan left there)
+// counts as zero; the merging wave resets the count, so replays of a captured
+// call with the same generation start from zero too.
+
+// Device-scope (sc1) 8-byte store and load of two floats.
+__device__ __forceinline__ void st_dev(float* p, float a, float b) {
+  __hip_atomic_store((unsigned long long*)p, __builtin_bit_cast(unsigned long long, make_float2(a, b)),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_dev(const float* p) {
+  return __builtin_bit_cast(float2, __hip_atomic_load((unsigned long long*)p, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Write this wave's partial of its rows to workspace slot `slot` with
+// device-scope stores (the wave waits for them before it counts the piece).
+template <int D>
+__device__ __forceinline__ void store_partial_dev(const Params& p, bool row_ok, const Acc<D>& A, float l,
+                                                  int64_t prow) {
+  constexpr int DT = D / 16;
+  const int g = (threadIdx.x & 63) >> 4;
+  if (row_ok) {
+    float* o = p.ws_o + prow * p.Dv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < DT; j += 2) st_dev(o + DT * (4 * g + i) + j, A.o[j][i], A.o[j + 1][i]);
+    if (g == 0) st_dev((float*)(p.ws_ml + prow), A.m, l);
+  }
+}
+
+// A cut piece whose count (and possibly the merge of its unit) waits until
+// the wave has streamed the rest of its share.
+struct Pending {
+  int b, kvh, w0, w1;
+  int64_t slot0;
+};
+
+// Count this piece on the unit's counter; true (on every lane) for the wave
+// that counts the last of `pieces`.  The compare-and-swap loop makes progress
+// whenever any of the unit's waves succeeds; its bound only guards against a
+// counter word that something else keeps changing.
+__device__ __forceinline__ bool count_piece(const Params& p, int unit, int pieces) {
+  int last = 0;
+  if ((threadIdx.x & 63) == 0) {
+    unsigned long long* c = p.ws_cnt + unit;
+    const unsigned long long gen = (unsigned long long)p.gen << 32;
+    // first try: this call's generation with nothing counted yet (right for
+    // the first wave to arrive); a failed swap returns the word to retry with
+    unsigned long long cur = gen;
+    for (int it = 0; it < (1 << 16); ++it) {
+      const unsigned long long next = (cur & ~0xffffffffull) == gen ? cur + 1 : gen | 1ull;
+      if (__hip_atomic_compare_exchange_strong(c, &cur, next, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)) {
+        last = (int)(next & 0xffffffffull) == pieces;
+        break;
+      }
+    }
+  }
+  last = __builtin_amdgcn_readfirstlane(last);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return last != 0;
+}
+
+// Merge the unit's pieces into the output, reading every slot (this wave's
+// own too) with device-scope loads in slot order -- so the sums, and the
+// output bits, do not depend on which wave happened to finish last -- then
+// reset the unit's count.  Slots: `slot0` for the first wave w0 of the unit,
+// then 2 w for every later wave up to w1.
+template <int QT, int D>
+__device__ __forceinline__ void merge_unit(const Params& p, const Pending& u) {
+  constexpr int DT = D / 16;
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  const bool row_ok = n < p.R;
+  const int64_t slot0 = u.slot0;
+  const int w0 = u.w0, w1 = u.w1;
+  float M = kNegInf, den = 0.f;
+  f32x4 acc[DT];
+#pragma unroll
+  for (int j = 0; j < DT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // slots in groups of kGroup: the group's loads are all issued before any is
+  // used, so a group costs one memory round trip
+  constexpr int kGroup = D >= 256 ? 1 : 256 / D;
+  for (int wb = w0; wb <= w1 && row_ok; wb += kGroup) {
+    float2 ml[kGroup];
+    f32x4 os[kGroup][DT];
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+      const int w = min(wb + k, w1);
+      const int64_t prow = (w == w0 ? slot0 : 2 * (int64_t)w) * p.R + n;
+      ml[k] = ld_dev((const float*)(p.ws_ml + prow));
+      const float* o = p.ws_o + prow * p.Dv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < DT; j += 2) {
+          const float2 v = ld_dev(o + DT * (4 * g + i) + j);
+          os[k][j][i] = v.x;
+          os[k][j + 1][i] = v.y;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+      if (wb + k > w1) break;
+      const float Mn = fmaxf(M, ml[k].x);
+      const float a1 = M == kNegInf ? 0.f : exp2f(M - Mn);
+      const float a2 = ml[k].x == kNegInf ? 0.f : exp2f(ml[k].x - Mn);
+      den = den * a1 + ml[k].y * a2;
+#pragma unroll
+      for (int j = 0; j < DT; ++j) acc[j] = acc[j] * a1 + os[k][j] * a2;
+      M = Mn;
+    }
+  }
+  if (row_ok) {
+    float num = 1.f;
+    if (p.sinks != nullptr) {
+      const float sk = p.sinks[u.kvh * p.G + n % p.G] * kLog2e;
+      const float Mf = fmaxf(M, sk);
+      num = M == kNegInf ? 0.f : exp2f(M - Mf);
+      den = den * num + exp2f(sk - Mf);
+    }
+    const float inv = den > 0.f ? p.out_scale * num / den : 0.f;
+    uint16_t* o = (uint16_t*)p.out + q_row_offset(p, u.b, u.kvh, n) * p.Dv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < DT; j += 4)
+        *(uint2*)(o + DT * (4 * g + i) + j) =
+            make_uint2(pack2<QT>(acc[j][i] * inv, acc[j + 1][i] * inv),
+                       pack2<QT>(acc[j + 2][i] * inv, acc[j + 3][i] * inv));
+  }
+  if (lane == 0)
+    __hip_atomic_store(p.ws_cnt + (u.b * p.Hkv + u.kvh), (unsigned long long)p.gen << 32,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Zero the outputs of the sequences with no visible token (they have no
+// tiles, so no wave meets them): wave w takes sequences w, w + W, ...
+__device__ __forceinline__ void zero_empty_units(const Params& p, const SkSched& S, int w, int W) {
+  const int lane = threadIdx.x & 63;
+  for (int b = w; b < p.B; b += W) {
+    int pre, n;
+    sk_seq_of(S, b, &pre, &n);
+    if (n != 0) continue;
+    for (int kvh = 0; kvh < p.Hkv; ++kvh)
+      for (int r = 0; r < p.R; ++r) {
+        uint16_t* o = (uint16_t*)p.out + q_row_offset(p, b, kvh, r) * p.Dv;
+        for (int d = 4 * lane; d < p.Dv; d += 256) *(uint2*)(o + d) = make_uint2(0u, 0u);
+      }
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void reset(Acc<D>& A) {
   A.m = kNegInf;
@@ -327,8 +491,12 @@ __global__ __launch_bounds__(64) void split_mfma16_kernel(Params p) {
 
 // Stream-K schedule: wave w of W takes an equal share of the tile stream of
 // all units; units wholly inside its share are finished here, the first and
-// the last (when cut) leave partials in workspace slots 2w and 2w+1.
-template <int QT, int KT, int D>
+// the last (when cut) leave partials in workspace slots 2w and 2w+1.  With
+// p.fused the wave that completes a cut unit merges it (see merge_unit);
+// otherwise the combine kernel does.
+// FUSED selects the single-launch merge at compile time, so the two-launch
+// kernel carries none of its code or registers.
+template <int QT, int KT, int D, bool FUSED>
 // (two waves per SIMD: the register budget keeps the accumulators in
 // architected VGPRs instead of moving them through AGPRs every tile)
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma16_sk_kernel(Params p) {
@@ -337,8 +505,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
   const int w = blockIdx.x, W = sk_waves_eff(S.T, gridDim.x);
   if (w >= W) return;
   const int64_t x0 = sk_wave_start(S.T, w, W), x1 = sk_wave_start(S.T, w + 1, W);
+  if (FUSED) zero_empty_units(p, S, w, W);
   Unit<KT, D> U;
   Acc<D> A;
+  // cut pieces (at most the share's first and last) counted after the loop,
+  // when their partial stores have long completed
+  Pending pend[2];
+  int npend = 0;
   for (int64_t x = x0; x < x1;) {
     const SkUnit u = sk_locate(p, S, x);
     const int64_t seg_end = min(x1, u.start + u.ntiles);
@@ -349,15 +522,38 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
     stream_tiles<QT, KT, D>(p, U, tile0 + (int)(x - u.start), tile0 + (int)(seg_end - u.start), A);
     const bool complete = x == u.start && seg_end == u.start + u.ntiles;
     const int slot = 2 * w + (x == x0 ? 0 : 1);
-    finish_unit<QT, KT, D>(p, U, A, complete, (int64_t)slot * p.R + (threadIdx.x & 15));
+    if (complete || !FUSED) {
+      finish_unit<QT, KT, D>(p, U, A, complete, (int64_t)slot * p.R + (threadIdx.x & 15));
+    } else {
+      const float l = sum_across_rows(A.l);
+      store_partial_dev<D>(p, U.row_ok, A, l, (int64_t)slot * p.R + (threadIdx.x & 15));
+      Pending& pd = pend[npend == 0 ? 0 : 1];
+      pd.b = u.b;
+      pd.kvh = u.kvh;
+      pd.w0 = sk_wave_of(S.T, u.start, W);
+      pd.w1 = sk_wave_of(S.T, u.start + u.ntiles - 1, W);
+      pd.slot0 = sk_wave_start(S.T, pd.w0, W) == u.start ? 2 * (int64_t)pd.w0 : 2 * (int64_t)pd.w0 + 1;
+      ++npend;
+    }
     x = seg_end;
+  }
+  if (FUSED && npend > 0) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the partial stores have completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    for (int k = 0; k < npend; ++k) {
+      const Pending& pd = pend[k];
+      if (count_piece(p, pd.b * p.Hkv + pd.kvh, pd.w1 - pd.w0 + 1)) merge_unit<QT, D>(p, pd);
+    }
   }
 }
 
 template <int QT, int KT, int D>
 hipError_t launch_split_mfma16(const Params& p, hipStream_t stream) {
-  if (p.sk_waves > 0) {
-    hipLaunchKernelGGL((split_mfma16_sk_kernel<QT, KT, D>), dim3(p.sk_waves), dim3(64), 0, stream, p);
+  if (p.sk_waves > 0 && p.fused) {
+    hipLaunchKernelGGL((split_mfma16_sk_kernel<QT, KT, D, true>), dim3(p.sk_waves), dim3(64), 0, stream, p);
+  } else if (p.sk_waves > 0) {
+    hipLaunchKernelGGL((split_mfma16_sk_kernel<QT, KT, D, false>), dim3(p.sk_waves), dim3(64), 0, stream, p);
   } else {
     dim3 grid(p.max_splits, p.Hkv, p.B);
     hipLaunchKernelGGL((split_mfma16_kernel<QT, KT, D>), grid, dim3(64), 0, stream, p);

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (pkv_\w+)", out))
     assert set(names) <= exported, set(names) - exported
-    assert pkv.lib().pkv_abi_version() == 2
+    assert pkv.lib().pkv_abi_version() == 3
 
 
 def test_struct_layouts_match_header(tmp_path):
@@ -53,7 +53,8 @@ int main(void) {
   printf("pkv_options %zu\\n", sizeof(pkv_options));
   printf("pkv_plan_info %zu\\n", sizeof(pkv_plan_info));
   F(pkv_dims, workspace_bytes) F(pkv_dims, kv_dtype) F(pkv_options, target_ctas) F(pkv_options, split_event) F(pkv_options, q_scale_dev) F(pkv_options, kv_scale_dev)
-  F(pkv_plan_info, workspace_bytes) F(pkv_plan_info, num_cus)
+  F(pkv_options, merge_mode)
+  F(pkv_plan_info, workspace_bytes) F(pkv_plan_info, num_cus) F(pkv_plan_info, single_launch)
   return 0;
 }
 """)
@@ -73,6 +74,8 @@ int main(void) {
     assert int(got["pkv_options.kv_scale_dev"]) == pkv.Options.kv_scale_dev.offset
     assert int(got["pkv_plan_info.workspace_bytes"]) == pkv.PlanInfo.workspace_bytes.offset
     assert int(got["pkv_plan_info.num_cus"]) == pkv.PlanInfo.num_cus.offset
+    assert int(got["pkv_options.merge_mode"]) == pkv.Options.merge_mode.offset
+    assert int(got["pkv_plan_info.single_launch"]) == pkv.PlanInfo.single_launch.offset
 
 
 BASE = dict(batch=64, num_q_heads=32, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
@@ -114,6 +117,24 @@ def test_plan_stream_k():
     assert plan(target_ctas=100)["ctas_per_split_grid"] == 100
     # batches above 256 fall back to the grid schedule
     assert plan(batch=300)["split_pages"] > 0
+
+
+def test_plan_single_launch_merge():
+    # the matrix-core stream-K plan can merge in the split kernel, with one
+    # 8-byte counter per (sequence, KV head) after the partials; by default
+    # it does when no wave's share can exceed 16 tiles; the split grid and
+    # the latent path keep the combine kernel
+    one, two = plan(single_launch=True), plan(single_launch=False)
+    assert one["single_launch"] == 1 and two["single_launch"] == 0
+    assert one["workspace_bytes"] >= two["workspace_bytes"] + 64 * 8 * 8
+    assert plan()["single_launch"] == 0                       # 8 K tokens: two launches
+    assert plan(pages_per_seq=2)["single_launch"] == 1        # 128 tokens: one launch
+    assert plan(pages_per_seq=4, target_ctas=64)["single_launch"] == 0
+    assert plan(batch=300, single_launch=True)["single_launch"] == 0
+    assert plan(split_pages=4, single_launch=True)["single_launch"] == 0
+    mla = plan(batch=32, num_q_heads=64, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
+               pages_per_seq=256, single_launch=True)
+    assert mla["single_launch"] == 0
 
 
 def test_plan_forced_split_and_workspace():

@@ -445,6 +445,62 @@ def test_repeated_calls_reuse_workspace():
         assert_parity(w, out, ref, "ws-reuse")
 
 
+# ---------------------------------------------------------------- single-launch merge
+
+def _ulps_apart(a, b, dtype):
+    """Largest distance between two outputs in units of the output dtype's
+    spacing at the larger magnitude."""
+    a, b = a.double().cpu(), b.double().cpu()
+    mant = {torch.bfloat16: 7, torch.float16: 10}[dtype]
+    e = torch.floor(torch.log2(torch.maximum(a.abs(), b.abs()).clamp(min=2.0 ** -14)))
+    return ((a - b).abs() / torch.exp2(e - mant)).max().item()
+
+
+@pytest.mark.parametrize("W", [0, 3, 64])
+@pytest.mark.parametrize("name", ["tiny", "gqa", "fp8", "spec"])
+def test_single_launch_matches_two_launches(name, W):
+    # the split kernel's own merge (the last wave of a unit) against the
+    # combine kernel on the same partials: both within the bound, and at most
+    # one output ulp apart (the merges sum in a different order)
+    w = SMALL[name]
+    print(f"[case] single-launch {name} waves={W}", flush=True)
+    inp = make(w, seed=90)
+    one = run_gpu(w, inp, target_ctas=W, single_launch=True)
+    two = run_gpu(w, inp, target_ctas=W, single_launch=False)
+    ref = run_oracle(w, inp)
+    assert_parity(w, one, ref, f"one-launch/{name}/W{W}")
+    assert_parity(w, two, ref, f"two-launch/{name}/W{W}")
+    assert _ulps_apart(one, two, w.q_dtype) <= 1.0
+    # the merge reads the slots in a fixed order, whichever wave finishes last
+    for _ in range(3):
+        assert torch.equal(run_gpu(w, inp, target_ctas=W, single_launch=True), one)
+
+
+def test_single_launch_sees_each_calls_partials():
+    # new queries on every call through one workspace: a merge that read a
+    # partial left by the previous call (a stale line in some cache) would
+    # differ from the two-launch result of the same call
+    w = SMALL["gqa"].replace(batch=4, seq_len_range=(300, 1500))
+    inp = make(w, seed=91)
+    plan = pkv.query_plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                          head_dim_qk=128, head_dim_v=128, pages_per_seq=inp["page_table"].shape[1],
+                          page_size=w.page_size, target_ctas=96, single_launch=True)
+    assert plan["single_launch"] == 1
+    ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(91)
+    for call in range(12):
+        inp["q"] = torch.randn(inp["q"].shape, generator=g, device=DEV).to(w.q_dtype)
+        one = torch.full((w.batch, 1, w.num_q_heads, 128), float("nan"), dtype=w.q_dtype, device=DEV)
+        pkv.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"],
+                        inp["seq_lens"], one, ws, num_kv_heads=w.num_kv_heads,
+                        page_size=w.page_size, kv_layout=w.kv_layout, target_ctas=96,
+                        single_launch=True)
+        two = run_gpu(w, inp, target_ctas=96, single_launch=False)
+        assert not torch.isnan(one).any(), f"call {call}: NaN"
+        assert _ulps_apart(one, two, w.q_dtype) <= 1.0, f"call {call}"
+    assert_parity(w, one, run_oracle(w, inp), "one-launch/last-call")
+
+
 # ---------------------------------------------------------------- latent (MLA) path
 
 MLA_SMALL = SMALL["mla"].replace(batch=3, seq_len_range=(1, 700))
