@@ -23,6 +23,12 @@ Reported (one JSON line on stdout):
 Algorithmic KV bytes = sum over sequences of (tokens some query row can see)
 x num_kv_heads x (head_dim_qk + head_dim_v) x element size; a latent cache
 row serves as K and V and counts once.
+
+    python bench.py --workload insert_prefill | insert_prefill_fp8 |
+                    insert_decode | insert_latent_decode
+
+times the cache write side instead (pkv_cache_insert: new tokens' rows into
+their slots): value = bytes read + bytes written per call / wall time.
 """
 from __future__ import annotations
 
@@ -96,6 +102,9 @@ def main():
               "attention shards over sequences and KV heads with no exchange; see the design "
               "notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload in INSERT_WORKLOADS:
+        return bench_insert(args)
 
     import paged_kv_attention_pages_amd as pkv
     from paged_kv_attention_pages_amd import synth
@@ -208,6 +217,94 @@ def main():
             "launch_us_mean": round(split_mean * 1e3, 2),
         },
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+# The write side (cache insert).  Shapes: the prefill inserts write one
+# 32 K-token prompt's K/V rows of the Llama-3-8B-shaped cache (8 KV heads,
+# head_dim 128, HND, 64-token pages); the decode inserts write one token per
+# sequence of the decode workloads (GQA: 64 sequences; latent: 32 sequences,
+# row [512 | 64] plus the 64-head query concat).
+INSERT_WORKLOADS = {
+    "insert_prefill": dict(N=32768, Hkv=8, Dk=128, Dlo=128, Dv=128, ps=64, layout="HND",
+                           cache=torch.bfloat16, Hq=0),
+    "insert_prefill_fp8": dict(N=32768, Hkv=8, Dk=128, Dlo=128, Dv=128, ps=64, layout="HND",
+                               cache=torch.float8_e4m3fn, Hq=0),
+    "insert_decode": dict(N=64, Hkv=8, Dk=128, Dlo=128, Dv=128, ps=64, layout="HND",
+                          cache=torch.bfloat16, Hq=0),
+    "insert_latent_decode": dict(N=32, Hkv=1, Dk=576, Dlo=512, Dv=0, ps=64, layout="NHD",
+                                 cache=torch.bfloat16, Hq=64),
+}
+
+
+def bench_insert(args):
+    import paged_kv_attention_pages_amd as pkv
+    cfg = INSERT_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    N, Hkv, Dk, Dlo, Dv, ps, Hq = (cfg[k] for k in ("N", "Hkv", "Dk", "Dlo", "Dv", "ps", "Hq"))
+    g = torch.Generator(device=dev).manual_seed(1)
+    P = 2 * (N + ps - 1) // ps + 1
+    shape = (lambda D: (P, ps, Hkv, D)) if cfg["layout"] == "NHD" else (lambda D: (P, Hkv, ps, D))
+    kc = torch.zeros(shape(Dk), dtype=cfg["cache"], device=dev)
+    vc = torch.zeros(shape(Dv), dtype=cfg["cache"], device=dev) if Dv else None
+    k = torch.randn(N, Hkv, Dlo, generator=g, device=dev).to(torch.bfloat16)
+    kr = torch.randn(N, Hkv, Dk - Dlo, generator=g, device=dev).to(torch.bfloat16) if Dlo < Dk else None
+    v = torch.randn(N, Hkv, Dv, generator=g, device=dev).to(torch.bfloat16) if Dv else None
+    slots = torch.randperm(P * ps, generator=torch.Generator().manual_seed(2))[:N].to(dev)
+    ql = torch.randn(N, Hq, Dlo, generator=g, device=dev).to(torch.bfloat16) if Hq else None
+    qh = torch.randn(N, Hq, Dk - Dlo, generator=g, device=dev).to(torch.bfloat16) if Hq else None
+    qo = torch.empty(N, Hq, Dk, dtype=torch.bfloat16, device=dev) if Hq else None
+    elem = 1 if cfg["cache"] == torch.float8_e4m3fn else 2
+    rows = N * Hkv * (Dk + Dv)
+    nbytes = rows * 2 + rows * elem + N * 8 + (N * Hq * Dk * 4 if Hq else 0)
+    # sources larger than a few MB rotate through replicas totalling >= 1 GB,
+    # so that each call reads them from HBM, not from the last-level cache
+    n_rep = min(16, max(1, math.ceil(1.0e9 / (rows * 2)))) if rows * 2 > (8 << 20) else 1
+    srcs = [(k, kr, v)] + [(k.clone(), None if kr is None else kr.clone(), None if v is None else v.clone())
+                           for _ in range(n_rep - 1)]
+
+    def call(i):
+        a, b, c = srcs[i % n_rep]
+        pkv.cache_insert(kc, vc, slots, a, k_rope=b, v=c, page_size=ps, kv_layout=cfg["layout"],
+                         cache_scale_inv=20.0 if elem == 1 else 1.0, q_lo=ql, q_hi=qh, q_out=qo)
+
+    K, W = args.steps, args.warmup
+    for i in range(W):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        call(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        call(i)
+        b.record()
+    torch.cuda.synchronize()
+    kern_ms = statistics.fmean(a.elapsed_time(b) for a, b in ev)
+    value = nbytes / (ms * 1e-3) / 1e9
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    print(f"[bench] {args.workload}: {ms * 1e3:.2f} us/call wall, evented {kern_ms * 1e3:.2f} us, "
+          f"{value:.0f} GB/s", file=sys.stderr, flush=True)
+    rec = {
+        "metric": "paged-cache insert GB/s (bytes read + written) + us/call",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" + ("->fp8" if elem == 1 else ""), "data": "synthetic",
+        "us_per_call": round(ms * 1e3, 2),
+        "config": {"workload": args.workload, "num_tokens": N, "num_kv_heads": Hkv,
+                   "head_dim_k": Dk, "head_dim_k_lo": Dlo, "head_dim_v": Dv, "page_size": ps,
+                   "kv_layout": cfg["layout"], "cache_dtype": str(cfg["cache"]).replace("torch.", ""),
+                   "query_concat_heads": Hq, "bytes_per_call": nbytes, "source_replicas": n_rep},
+        "roofline": {"kernel": "cache insert", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": nbytes,
+                     "launch_us_mean": round(kern_ms * 1e3, 2)},
+        "cpu_baseline": None,
     }
     print(json.dumps(rec), flush=True)
 

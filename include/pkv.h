@@ -219,6 +219,51 @@ pkv_status pkv_validate_inputs(const int32_t* page_table, const uint32_t* seq_le
                                int num_kv_heads, int page_size, int window,
                                int q_seq_len, void* stream, const pkv_dims* dims);
 
+/* ---- the write side of the paged cache ------------------------------ */
+
+/* Sizes of a cache insert. */
+typedef struct pkv_insert_dims {
+  int32_t num_tokens;     /* N: rows to insert (slot_mapping.shape[0])      */
+  int32_t num_kv_heads;   /* Hkv                                            */
+  int32_t head_dim_k;     /* cache K row width Dk (multiple of 8)           */
+  int32_t head_dim_k_lo;  /* leading part of the K row from k_src; the rest
+                             (Dk - Dlo, from k_rope_src) -- Dlo == Dk: no
+                             second source; multiple of 8                   */
+  int32_t head_dim_v;     /* V row width (multiple of 8); 0: no V cache     */
+  int32_t page_size;      /* 16, 32, 64 or 128                              */
+  int32_t num_pages;      /* physical pages of the cache                    */
+  int32_t layout;         /* pkv_layout                                     */
+  int32_t src_dtype;      /* PKV_F16 or PKV_BF16: k_src, k_rope_src, v_src,
+                             q_lo, q_hi, q_out                              */
+  int32_t cache_dtype;    /* == src_dtype, or PKV_FP8_E4M3                  */
+  int32_t num_q_heads;    /* query concat heads (used when q_out != NULL)   */
+} pkv_insert_dims;
+
+/* Inserts new tokens' rows into the paged cache (vLLM Kimi-K3 MLA page,
+ * `_decode_concat_cache`: the decode step's latent cache insert at
+ * slot_mapping, fused with the query concat [ql_nope | q_pe]).
+ *   For token i with slot s = slot_mapping[i] (int64; page s / page_size,
+ *   offset s % page_size) and KV head h:
+ *     K row  = [k_src[i, h, 0:Dlo] | k_rope_src[i, h, 0:Dk-Dlo]]
+ *     V row  = v_src[i, h, 0:Dv]
+ *   stored at [page, offset, h] (NHD) or [page, h, offset] (HND).  A slot
+ *   below 0 (padding) or at/after num_pages * page_size writes nothing.
+ *   A 16-bit cache gets the source bits; an E4M3 cache gets the nearest
+ *   E4M3 value of the binary32 product x * cache_scale_inv (ties to even,
+ *   magnitudes past 448 saturate to 448).  cache_scale_inv_dev, when not
+ *   NULL, points at the scale in device memory (read when the kernel runs)
+ *   and replaces cache_scale_inv.
+ *   When q_out is not NULL: q_out[i, h] = [q_lo[i, h, 0:Dlo] | q_hi[i, h,
+ *   0:Dk-Dlo]] for h < num_q_heads (all [N, Hq, .] contiguous, src_dtype).
+ * The latent cache is Hkv = 1, Dk = 576, Dlo = 512, Dv = 0 (V is the
+ * leading 512 entries of the K row).  All tensors are contiguous device
+ * memory, 16-byte aligned; one launch on `stream`; errors as for decode. */
+pkv_status pkv_cache_insert(const void* k_src, const void* k_rope_src, const void* v_src,
+                            const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                            float cache_scale_inv, const float* cache_scale_inv_dev,
+                            const void* q_lo, const void* q_hi, void* q_out, void* stream,
+                            const pkv_insert_dims* dims);
+
 #ifdef __cplusplus
 }
 #endif

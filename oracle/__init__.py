@@ -45,6 +45,17 @@ class _Problem(ctypes.Structure):
     ]
 
 
+class _Insert(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int), ("num_kv_heads", ctypes.c_int),
+        ("head_dim_k", ctypes.c_int), ("head_dim_k_lo", ctypes.c_int),
+        ("head_dim_v", ctypes.c_int), ("page_size", ctypes.c_int),
+        ("num_pages", ctypes.c_int), ("layout", ctypes.c_int),
+        ("src_dtype", ctypes.c_int), ("cache_dtype", ctypes.c_int),
+        ("cache_scale_inv", ctypes.c_float),
+    ]
+
+
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (plain C, fp64, OpenMP, no fast-math)."""
     with _lock:
@@ -69,6 +80,10 @@ def _load():
         lib.pkvo_decode.restype = ctypes.c_int
         lib.pkvo_decode.argtypes = [ctypes.POINTER(_Problem)] + [ctypes.c_void_p] * 8
         lib.pkvo_max_threads.restype = ctypes.c_int
+        lib.pkvo_encode_e4m3fn.restype = ctypes.c_uint8
+        lib.pkvo_encode_e4m3fn.argtypes = [ctypes.c_float]
+        lib.pkvo_cache_insert.restype = ctypes.c_int
+        lib.pkvo_cache_insert.argtypes = [ctypes.POINTER(_Insert)] + [ctypes.c_void_p] * 6
         _lib = lib
     return _lib
 
@@ -145,3 +160,39 @@ def decode(q, k_cache, v_cache, page_table, seq_lens, *, num_kv_heads, page_size
     if rc > 0:
         raise ValueError(f"oracle: sequence {rc - 1} needs a page id outside [0, num_pages)")
     return torch.from_numpy(out)
+
+
+def encode_e4m3fn(x: float) -> int:
+    """E4M3 code of the binary32 value nearest to x (ties to even, saturating at 448)."""
+    return _load().pkvo_encode_e4m3fn(x)
+
+
+def cache_insert(k_cache, v_cache, slot_mapping, k, k_rope=None, v=None, *, page_size,
+                 kv_layout="NHD", cache_scale_inv=1.0):
+    """The write side: new tokens' rows into copies of the caches at slot_mapping.
+
+    k [N, Hkv, Dlo] (16-bit), k_rope [N, Hkv, Dk - Dlo] or None, v [N, Hkv, Dv] or
+    None (latent cache), slot_mapping [N] int64.  Returns host copies of the
+    updated (k_cache, v_cache) with the input caches' dtypes.
+    """
+    N = slot_mapping.shape[0]
+    Hkv = k.shape[-2]
+    Dlo = k.shape[-1]
+    Dk = k_cache.shape[-1]
+    Dv = 0 if v is None else v.shape[-1]
+    p = _Insert()
+    p.num_tokens, p.num_kv_heads, p.head_dim_k, p.head_dim_k_lo, p.head_dim_v = N, Hkv, Dk, Dlo, Dv
+    p.page_size, p.num_pages, p.layout = page_size, k_cache.shape[0], LAYOUT_CODE[kv_layout]
+    p.src_dtype, p.cache_dtype = DTYPE_CODE[k.dtype], DTYPE_CODE[k_cache.dtype]
+    p.cache_scale_inv = float(cache_scale_inv)
+    kc = k_cache.detach().to("cpu").clone()
+    vc = None if v_cache is None else v_cache.detach().to("cpu").clone()
+    ka, ra, va = _raw(k), None if k_rope is None else _raw(k_rope), None if v is None else _raw(v)
+    sm = np.ascontiguousarray(slot_mapping.detach().cpu().to(torch.int64).numpy())
+    kc_raw = kc.view(torch.int16 if kc.element_size() == 2 else torch.uint8).numpy()
+    vc_raw = None if vc is None else vc.view(torch.int16 if vc.element_size() == 2 else torch.uint8).numpy()
+    rc = _load().pkvo_cache_insert(ctypes.byref(p), _ptr(ka), _ptr(ra), _ptr(va), _ptr(sm),
+                                   _ptr(kc_raw), _ptr(vc_raw))
+    if rc < 0:
+        raise ValueError("oracle: malformed insert sizes")
+    return kc, vc

@@ -278,3 +278,109 @@ int pkvo_max_threads(void)
   return 1;
 #endif
 }
+
+/* ==================================================================== */
+/* The cache write side: insert the new tokens' rows at slot_mapping.   */
+/*                                                                      */
+/* vLLM `models/kimi_k3/nvidia/mla` page, `_decode_concat_cache`: one   */
+/* fused step builds the decode query [ql_nope | q_pe] and writes each  */
+/* new token's latent row [kv_c_normed | k_pe] into the paged cache at  */
+/* its slot_mapping entry; a quantised (fp8) cache stores the row times */
+/* `cache_scale_inv` (the reciprocal of the cache scale, `_k_scale_inv`,*/
+/* precomputed in `process_weights_after_loading`).  The same write for */
+/* a K/V cache (the xqa page's k_cache / v_cache layouts) is the step   */
+/* just before decode attention.                                        */
+/*                                                                      */
+/* Readings (listed in the design notes):                               */
+/*   - a slot is page * page_size + offset; a negative slot (padding)   */
+/*     or one past num_pages * page_size writes nothing;                */
+/*   - a 16-bit cache of the source dtype receives the source bits;     */
+/*   - an E4M3 cache receives the nearest E4M3 value (ties to the even  */
+/*     code) of the binary32 product value * cache_scale_inv, with      */
+/*     magnitudes beyond the largest finite value 448 stored as +-448   */
+/*     (saturation) and NaN as S.1111.111.                              */
+/* ==================================================================== */
+
+/* OCP E4M3 ("fn") encoder, by definition: the representable value nearest
+ * to x (searched over every finite code), ties to the code with an even
+ * last fraction bit; |x| >= 448 saturates to 448; NaN gives 0x7F. */
+uint8_t pkvo_encode_e4m3fn(float xf)
+{
+  const double x = (double)xf;
+  if (isnan(x))
+    return 0x7f;
+  const int s = signbit(x) ? 0x80 : 0;
+  const double a = fabs(x);
+  if (a >= 448.0)
+    return (uint8_t)(s | 0x7e);
+  int best = 0;
+  double bd = a; /* distance to code 0 (+0) */
+  for (int c = 1; c <= 0x7e; ++c) {
+    const double d = fabs(pkvo_decode_e4m3fn((uint8_t)c) - a);
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      best = c;
+      bd = d;
+    }
+  }
+  return (uint8_t)(s | best);
+}
+
+typedef struct pkvo_insert {
+  int num_tokens, num_kv_heads;
+  int head_dim_k;    /* cache K row width                                   */
+  int head_dim_k_lo; /* leading part of the K row from k_src; the rest from k_rope */
+  int head_dim_v;    /* V row width; 0: no V cache (latent cache)            */
+  int page_size, num_pages, layout;
+  int src_dtype, cache_dtype;
+  float cache_scale_inv;
+} pkvo_insert;
+
+static size_t insert_index(const pkvo_insert *p, int64_t page, int off, int h, int D, int d)
+{
+  if (p->layout == PKVO_NHD)
+    return (((size_t)page * p->page_size + off) * p->num_kv_heads + h) * D + d;
+  return (((size_t)page * p->num_kv_heads + h) * p->page_size + off) * D + d;
+}
+
+static void insert_elem(const pkvo_insert *p, void *cache, size_t idx, uint16_t bits)
+{
+  if (p->cache_dtype == PKVO_E4M3) {
+    const double v = p->src_dtype == PKVO_F16 ? pkvo_decode_f16(bits) : pkvo_decode_bf16(bits);
+    const float y = (float)v * p->cache_scale_inv; /* one binary32 rounding */
+    ((uint8_t *)cache)[idx] = pkvo_encode_e4m3fn(y);
+  } else {
+    ((uint16_t *)cache)[idx] = bits;
+  }
+}
+
+/* k_src [N, Hkv, Dlo], k_rope [N, Hkv, Dk - Dlo] (NULL when Dlo == Dk),
+ * v_src [N, Hkv, Dv] (NULL when Dv == 0), slot_mapping [N].  Returns 0, or
+ * -1 for malformed sizes. */
+int pkvo_cache_insert(const pkvo_insert *p, const uint16_t *k_src, const uint16_t *k_rope,
+                      const uint16_t *v_src, const int64_t *slot_mapping, void *k_cache,
+                      void *v_cache)
+{
+  if (p->num_tokens < 0 || p->num_kv_heads < 1 || p->head_dim_k < 1 ||
+      p->head_dim_k_lo < 1 || p->head_dim_k_lo > p->head_dim_k || p->head_dim_v < 0 ||
+      p->page_size < 1 || p->num_pages < 1)
+    return -1;
+  const int H = p->num_kv_heads, Dk = p->head_dim_k, Dlo = p->head_dim_k_lo, Dv = p->head_dim_v;
+  for (int i = 0; i < p->num_tokens; ++i) {
+    const int64_t s = slot_mapping[i];
+    if (s < 0 || s >= (int64_t)p->num_pages * p->page_size)
+      continue;
+    const int64_t page = s / p->page_size;
+    const int off = (int)(s % p->page_size);
+    for (int h = 0; h < H; ++h) {
+      for (int d = 0; d < Dk; ++d) {
+        const uint16_t bits = d < Dlo ? k_src[((size_t)i * H + h) * Dlo + d]
+                                      : k_rope[((size_t)i * H + h) * (Dk - Dlo) + (d - Dlo)];
+        insert_elem(p, k_cache, insert_index(p, page, off, h, Dk, d), bits);
+      }
+      for (int d = 0; d < Dv; ++d)
+        insert_elem(p, v_cache, insert_index(p, page, off, h, Dv, d),
+                    v_src[((size_t)i * H + h) * Dv + d]);
+    }
+  }
+  return 0;
+}

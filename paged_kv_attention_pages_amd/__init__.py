@@ -56,6 +56,15 @@ class Options(ctypes.Structure):
                 ("kv_scale_dev", ctypes.c_void_p), ("merge_mode", ctypes.c_int32)]
 
 
+class InsertDims(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim_k", ctypes.c_int32), ("head_dim_k_lo", ctypes.c_int32),
+                ("head_dim_v", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("src_dtype", ctypes.c_int32), ("cache_dtype", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32)]
+
+
 class PlanInfo(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("split_pages", ctypes.c_int32),
                 ("max_splits", ctypes.c_int32), ("rows", ctypes.c_int32),
@@ -101,6 +110,9 @@ def lib():
                 L.pkv_validate_inputs.restype = ctypes.c_int
                 L.pkv_validate_inputs.argtypes = [_vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                   ctypes.c_int, _vp, ctypes.POINTER(Dims)]
+                L.pkv_cache_insert.restype = ctypes.c_int
+                L.pkv_cache_insert.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
+                                               _vp, _vp, _vp, _vp, ctypes.POINTER(InsertDims)]
                 _lib = L
     return _lib
 
@@ -298,3 +310,84 @@ def validate_inputs(q, k_cache, page_table, seq_lens, *, num_kv_heads, page_size
     _check(lib().pkv_validate_inputs(_ptr(page_table), _ptr(seq_lens), num_kv_heads, page_size,
                                      sliding_win_size, q_seq_len, ctypes.c_void_p(stream),
                                      ctypes.byref(d)))
+
+
+def cache_insert(k_cache, v_cache, slot_mapping, k, k_rope=None, v=None, *, page_size,
+                 kv_layout="NHD", cache_scale_inv=1.0, q_lo=None, q_hi=None, q_out=None,
+                 stream=None):
+    """Write new tokens' rows into the paged cache, in place (one launch).
+
+    k [N, Hkv, Dlo] (and k_rope [N, Hkv, Dk - Dlo] for a K row built from two
+    parts, as the latent row [kv_c_normed | k_pe]); v [N, Hkv, Dv] or None for
+    a latent cache (v_cache None); slot_mapping [N] int64 (page * page_size +
+    offset, negative = padding).  A float8_e4m3fn (or uint8) cache stores
+    round(x * cache_scale_inv); ``cache_scale_inv`` is a float or a
+    one-element float32 device tensor.  With q_out [N, Hq, Dk], also writes
+    the query concat [q_lo | q_hi].  Returns k_cache.
+    """
+    if k.device.type != "cuda":
+        raise PkvError(1, "cache_insert runs on the GPU only")
+    if k.dtype not in (torch.float16, torch.bfloat16):
+        raise PkvError(1, f"source dtype must be float16 or bfloat16, got {k.dtype}")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("slot_mapping", slot_mapping),
+                    ("k", k), ("k_rope", k_rope), ("v", v), ("q_lo", q_lo), ("q_hi", q_hi),
+                    ("q_out", q_out)):
+        if t is None:
+            continue
+        if not t.is_contiguous():
+            raise PkvError(1, f"{name} must be contiguous")
+        if t.device != k.device:
+            raise PkvError(1, f"{name} is on {t.device}, k on {k.device}")
+    for name, t in (("k_rope", k_rope), ("v", v), ("q_lo", q_lo), ("q_hi", q_hi), ("q_out", q_out)):
+        if t is not None and t.dtype != k.dtype:
+            raise PkvError(1, f"{name} dtype {t.dtype} differs from k's {k.dtype}")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1:
+        raise PkvError(1, "slot_mapping must be a 1-D int64 tensor")
+    if k_cache.dtype not in _DTYPE or (v_cache is not None and v_cache.dtype != k_cache.dtype):
+        raise PkvError(1, "caches must share one supported dtype")
+    N = slot_mapping.shape[0]
+    Dk = k_cache.shape[-1]
+    if k.dim() != 3 or k.shape[0] != N:
+        raise PkvError(1, f"k must be [N, num_kv_heads, Dlo] with N = {N}")
+    Hkv, Dlo = k.shape[1], k.shape[2]
+    kv_layout = kv_layout.upper()
+    if kv_layout not in _LAYOUT:
+        raise PkvError(1, f"kv_layout must be NHD or HND, got {kv_layout}")
+    heads_at = 2 if kv_layout == "NHD" else 1
+    slots_at = 1 if kv_layout == "NHD" else 2
+    if (k_cache.dim() != 4 or k_cache.shape[heads_at] != Hkv or k_cache.shape[slots_at] != page_size):
+        raise PkvError(1, f"k_cache must be [pages, {page_size}, {Hkv}, Dk] (NHD) or "
+                          f"[pages, {Hkv}, {page_size}, Dk] (HND); got {tuple(k_cache.shape)}")
+    if (k_rope is None) != (Dlo == Dk):
+        raise PkvError(1, "k_rope is needed exactly when k is narrower than the cache row")
+    if k_rope is not None and tuple(k_rope.shape) != (N, Hkv, Dk - Dlo):
+        raise PkvError(1, f"k_rope must be [{N}, {Hkv}, {Dk - Dlo}]")
+    Dv = 0
+    if v is not None or v_cache is not None:
+        if v is None or v_cache is None or v_cache.shape[:3] != k_cache.shape[:3]:
+            raise PkvError(1, "v and v_cache go together, with k_cache's first three dims")
+        Dv = v_cache.shape[-1]
+        if tuple(v.shape) != (N, Hkv, Dv):
+            raise PkvError(1, f"v must be [{N}, {Hkv}, {Dv}]")
+    Hq = 0
+    if q_out is not None:
+        if q_out.dim() != 3 or q_out.shape[0] != N or q_out.shape[2] != Dk:
+            raise PkvError(1, f"q_out must be [{N}, num_q_heads, {Dk}]")
+        Hq = q_out.shape[1]
+        if q_lo is None or tuple(q_lo.shape) != (N, Hq, Dlo):
+            raise PkvError(1, f"q_lo must be [{N}, {Hq}, {Dlo}]")
+        if Dlo < Dk and (q_hi is None or tuple(q_hi.shape) != (N, Hq, Dk - Dlo)):
+            raise PkvError(1, f"q_hi must be [{N}, {Hq}, {Dk - Dlo}]")
+    d = InsertDims(N, Hkv, Dk, Dlo, Dv, page_size, k_cache.shape[0], _LAYOUT[kv_layout],
+                   _DTYPE[k.dtype], _DTYPE[k_cache.dtype], Hq)
+    scale, scale_dev = _scale_arg(cache_scale_inv, "cache_scale_inv", k.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(k.device).cuda_stream
+    with torch.cuda.device(k.device):
+        st = lib().pkv_cache_insert(_ptr(k), _ptr(k_rope), _ptr(v), _ptr(slot_mapping),
+                                    _ptr(k_cache), _ptr(v_cache), float(scale),
+                                    None if scale_dev is None else ctypes.c_void_p(scale_dev),
+                                    _ptr(q_lo), _ptr(q_hi), _ptr(q_out), ctypes.c_void_p(stream),
+                                    ctypes.byref(d))
+    _check(st)
+    return k_cache

@@ -18,7 +18,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "split_mfma.hip", "split_mla.hip", "split_valu.hip", "combine.hip"]
+SOURCES = ["api.hip", "split_mfma.hip", "split_mla.hip", "split_valu.hip", "combine.hip",
+           "cache_insert.hip"]
 LIB = os.path.join(HERE, "libpkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 

@@ -438,4 +438,81 @@ pkv_status pkv_validate_inputs(const int32_t* page_table, const uint32_t* seq_le
   return PKV_OK;
 }
 
+pkv_status pkv_cache_insert(const void* k_src, const void* k_rope_src, const void* v_src,
+                            const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                            float cache_scale_inv, const float* cache_scale_inv_dev,
+                            const void* q_lo, const void* q_hi, void* q_out, void* stream,
+                            const pkv_insert_dims* d) {
+  if (d == nullptr) return fail(PKV_ERR_INVALID_ARGUMENT, "dims is NULL");
+  if (d->num_tokens < 0) return fail(PKV_ERR_INVALID_ARGUMENT, "num_tokens must be >= 0");
+  if (d->num_kv_heads < 1) return fail(PKV_ERR_INVALID_ARGUMENT, "num_kv_heads must be >= 1");
+  const int Dk = d->head_dim_k, Dlo = d->head_dim_k_lo, Dv = d->head_dim_v;
+  if (Dk < 8 || Dk % 8 || Dlo < 8 || Dlo % 8 || Dlo > Dk || Dv < 0 || Dv % 8)
+    return fail(PKV_ERR_INVALID_ARGUMENT,
+                "head dims must be multiples of 8 with 8 <= head_dim_k_lo <= head_dim_k "
+                "(got k %d, k_lo %d, v %d)", Dk, Dlo, Dv);
+  const int ps = d->page_size;
+  if (ps != 16 && ps != 32 && ps != 64 && ps != 128)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "page_size must be one of 16, 32, 64, 128; got %d", ps);
+  if (d->num_pages < 1) return fail(PKV_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+  if (d->layout != PKV_NHD && d->layout != PKV_HND)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "kv_layout must be NHD (0) or HND (1); got %d", d->layout);
+  if (d->src_dtype != PKV_F16 && d->src_dtype != PKV_BF16)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "source dtype must be float16 or bfloat16; got %d",
+                d->src_dtype);
+  if (d->cache_dtype != d->src_dtype && d->cache_dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_INVALID_ARGUMENT,
+                "cache dtype must equal the source dtype or be float8_e4m3fn; got %d for %d",
+                d->cache_dtype, d->src_dtype);
+  if (q_out != nullptr && (d->num_q_heads < 1 || q_lo == nullptr || (Dlo < Dk && q_hi == nullptr)))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "the query concat needs num_q_heads >= 1, q_lo and "
+                                          "(when head_dim_k_lo < head_dim_k) q_hi");
+  if (!std::isfinite(cache_scale_inv))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "cache_scale_inv must be finite");
+  if (d->num_tokens == 0) {
+    g_err.clear();
+    return PKV_OK;
+  }
+  if (!k_src || !slot_mapping || !k_cache || (Dlo < Dk && !k_rope_src) || (Dv > 0 && (!v_src || !v_cache)))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "k_src, slot_mapping, k_cache (and k_rope_src when "
+                                          "head_dim_k_lo < head_dim_k, v_src and v_cache when "
+                                          "head_dim_v > 0) must not be NULL");
+  for (const void* ptr : {k_src, k_rope_src, v_src, (const void*)k_cache, (const void*)v_cache, q_lo,
+                          q_hi, (const void*)q_out})
+    if (misaligned(ptr, 16))
+      return fail(PKV_ERR_INVALID_ARGUMENT, "insert tensors must be 16-byte aligned");
+  if (misaligned(slot_mapping, 8) || misaligned(cache_scale_inv_dev, 4))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "slot_mapping must be 8-byte and the device scale "
+                                          "4-byte aligned");
+  pkv::InsertParams p{};
+  p.k_src = k_src;
+  p.k_rope = k_rope_src;
+  p.v_src = v_src;
+  p.slot_mapping = slot_mapping;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.q_lo = q_lo;
+  p.q_hi = q_hi;
+  p.q_out = q_out;
+  p.N = d->num_tokens;
+  p.Hkv = d->num_kv_heads;
+  p.Hq = q_out != nullptr ? d->num_q_heads : 0;
+  p.Dk = Dk;
+  p.Dlo = Dlo;
+  p.Dv = Dv;
+  p.ps = ps;
+  p.num_pages = d->num_pages;
+  p.layout = d->layout;
+  p.scale_inv = cache_scale_inv;
+  p.scale_inv_dev = cache_scale_inv_dev;
+  const int64_t items = (int64_t)p.N * std::max<int64_t>((int64_t)p.Hkv * std::max(Dk, Dv), (int64_t)p.Hq * Dk) / 8;
+  if (items >= ((int64_t)1 << 31))
+    return fail(PKV_ERR_UNSUPPORTED, "insert too large: %lld 16-byte items in one part (limit 2^31)",
+                (long long)items);
+  const hipError_t e = pkv::launch_cache_insert(d->src_dtype, d->cache_dtype, p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "cache insert launch failed: %s", hipGetErrorString(e));
+  g_err.clear();
+  return PKV_OK;
+}
+
 }  // extern "C"

@@ -18,6 +18,23 @@ hipError_t launch_split_mla(int q_dtype, const Params& p, hipStream_t s);
 // Split-KV decode on the vector ALUs, up to 8 rows per KV head.
 hipError_t launch_split_valu(int q_dtype, int kv_dtype, int D, const Params& p, hipStream_t s);
 
+// The write side: new tokens' rows into the paged cache at their slots.
+struct InsertParams {
+  const void* k_src;          // [N, Hkv, Dlo]
+  const void* k_rope;         // [N, Hkv, Dk - Dlo] (or unused when Dlo == Dk)
+  const void* v_src;          // [N, Hkv, Dv] (Dv == 0: no V cache)
+  const int64_t* slot_mapping;  // [N]; < 0 or past the pool: skipped
+  void* k_cache;
+  void* v_cache;
+  const void* q_lo;           // [N, Hq, Dlo]   query concat (q_out == null: none)
+  const void* q_hi;           // [N, Hq, Dk - Dlo]
+  void* q_out;                // [N, Hq, Dk]
+  int N, Hkv, Hq, Dk, Dlo, Dv, ps, num_pages, layout;
+  float scale_inv;            // E4M3 cache: stored value = round(x * scale_inv)
+  const float* scale_inv_dev; // device-resident scale_inv, or null
+};
+hipError_t launch_cache_insert(int src_dtype, int cache_dtype, const InsertParams& p, hipStream_t s);
+
 // Log-sum-exp merge of the split partials of every sequence that needed
 // more than one split (zeros for sequences with nothing visible).
 hipError_t launch_combine(int q_dtype, const Params& p, hipStream_t s);

@@ -54,6 +54,8 @@ int main(void) {
   printf("pkv_plan_info %zu\\n", sizeof(pkv_plan_info));
   F(pkv_dims, workspace_bytes) F(pkv_dims, kv_dtype) F(pkv_options, target_ctas) F(pkv_options, split_event) F(pkv_options, q_scale_dev) F(pkv_options, kv_scale_dev)
   F(pkv_options, merge_mode)
+  printf("pkv_insert_dims %zu\\n", sizeof(pkv_insert_dims));
+  F(pkv_insert_dims, num_q_heads) F(pkv_insert_dims, cache_dtype)
   F(pkv_plan_info, workspace_bytes) F(pkv_plan_info, num_cus) F(pkv_plan_info, single_launch)
   return 0;
 }
@@ -75,6 +77,9 @@ int main(void) {
     assert int(got["pkv_plan_info.workspace_bytes"]) == pkv.PlanInfo.workspace_bytes.offset
     assert int(got["pkv_plan_info.num_cus"]) == pkv.PlanInfo.num_cus.offset
     assert int(got["pkv_options.merge_mode"]) == pkv.Options.merge_mode.offset
+    assert int(got["pkv_insert_dims"]) == ctypes.sizeof(pkv.InsertDims)
+    assert int(got["pkv_insert_dims.num_q_heads"]) == pkv.InsertDims.num_q_heads.offset
+    assert int(got["pkv_insert_dims.cache_dtype"]) == pkv.InsertDims.cache_dtype.offset
     assert int(got["pkv_plan_info.single_launch"]) == pkv.PlanInfo.single_launch.offset
 
 
@@ -217,3 +222,42 @@ def test_binding_rejects_cpu_tensors():
         pkv.decode_attn(q, k, k, torch.zeros(2, 4, dtype=torch.int32),
                         torch.zeros(2, dtype=torch.int32), torch.empty_like(q),
                         num_kv_heads=1, page_size=16)
+
+
+def _insert_dims(**kw):
+    d = dict(num_tokens=4, num_kv_heads=2, head_dim_k=128, head_dim_k_lo=128, head_dim_v=128,
+             page_size=16, num_pages=8, layout=0, src_dtype=1, cache_dtype=1, num_q_heads=0)
+    d.update(kw)
+    return pkv.InsertDims(**d)
+
+
+@pytest.mark.parametrize("kw, msg", [
+    (dict(head_dim_k=100), "multiples of 8"),
+    (dict(head_dim_k_lo=136), "multiples of 8"),
+    (dict(head_dim_v=12), "multiples of 8"),
+    (dict(page_size=8), "page_size"),
+    (dict(layout=3), "kv_layout"),
+    (dict(src_dtype=2), "source dtype"),
+    (dict(cache_dtype=0), "cache dtype"),
+    (dict(num_kv_heads=0), "num_kv_heads"),
+    (dict(num_tokens=-1), "num_tokens"),
+])
+def test_cache_insert_rejects_bad_sizes(kw, msg):
+    # checked on the host before any device call
+    L = pkv.lib()
+    st = L.pkv_cache_insert(None, None, None, None, None, None, 1.0, None, None, None, None, None,
+                            ctypes.byref(_insert_dims(**kw)))
+    assert st == 1 and msg in L.pkv_last_error().decode()
+
+
+def test_cache_insert_null_tensors_and_bad_scale():
+    L = pkv.lib()
+    st = L.pkv_cache_insert(None, None, None, None, None, None, 1.0, None, None, None, None, None,
+                            ctypes.byref(_insert_dims()))
+    assert st == 1 and "must not be NULL" in L.pkv_last_error().decode()
+    st = L.pkv_cache_insert(None, None, None, None, None, None, float("inf"), None, None, None,
+                            None, None, ctypes.byref(_insert_dims()))
+    assert st == 1 and "finite" in L.pkv_last_error().decode()
+    # nothing to insert: no device call, success
+    assert L.pkv_cache_insert(None, None, None, None, None, None, 1.0, None, None, None, None, None,
+                              ctypes.byref(_insert_dims(num_tokens=0))) == 0

@@ -435,3 +435,138 @@ def test_poison_makes_stray_reads_visible():
     got = run_oracle(w, inp2)
     assert torch.isnan(got[0]).all()
     assert torch.isfinite(got[1:]).all()
+
+
+# ---------------------------------------------------------------- write side (cache insert)
+
+def test_e4m3_encoder_round_trips_every_finite_code():
+    # encode(decode(c)) == c for every finite code of the format definition
+    for c in range(256):
+        v = oracle.decode_e4m3fn(c)
+        if math.isnan(v):
+            continue
+        assert oracle.encode_e4m3fn(v) == c, hex(c)
+
+
+def test_e4m3_encoder_rounds_to_nearest_ties_to_even_and_saturates():
+    codes = [c for c in range(0x7f)]                       # +0 .. 448, increasing
+    vals = [oracle.decode_e4m3fn(c) for c in codes]
+    for c in codes[:-1]:
+        lo, hi = vals[c], vals[c + 1]
+        mid = np.float32((lo + hi) / 2)                    # exact in binary32
+        assert float(mid) == (lo + hi) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.encode_e4m3fn(float(mid)) == even, hex(c)
+        assert oracle.encode_e4m3fn(float(np.nextafter(mid, np.float32(0)))) == c
+        assert oracle.encode_e4m3fn(float(np.nextafter(mid, np.float32(1e9)))) == c + 1
+        assert oracle.encode_e4m3fn(-float(mid)) == 0x80 | even
+    assert oracle.encode_e4m3fn(448.0) == 0x7E
+    assert oracle.encode_e4m3fn(464.0) == 0x7E             # the midpoint to the next (absent) step
+    assert oracle.encode_e4m3fn(1e30) == 0x7E and oracle.encode_e4m3fn(-1e30) == 0xFE
+    assert oracle.encode_e4m3fn(float("inf")) == 0x7E
+    assert oracle.encode_e4m3fn(float("nan")) == 0x7F
+    assert oracle.encode_e4m3fn(-0.0) == 0x80 and oracle.encode_e4m3fn(0.0) == 0x00
+
+
+def test_e4m3_encoder_matches_torch_cast_in_range():
+    # torch's float8_e4m3fn cast rounds to nearest even (it gives NaN past 448)
+    g = torch.Generator().manual_seed(5)
+    x = torch.cat([torch.randn(20000, generator=g) * 40, torch.rand(2000, generator=g) * 2e-3])
+    x = x[x.abs() < 448]
+    ours = torch.tensor([oracle.encode_e4m3fn(float(v)) for v in x], dtype=torch.uint8)
+    assert torch.equal(ours, x.to(torch.float8_e4m3fn).view(torch.uint8))
+
+
+def _insert_case(layout, cache_dtype=torch.bfloat16, N=5, Hkv=2, D=16, ps=4, P=9, seed=3):
+    g = torch.Generator().manual_seed(seed)
+    kc = (torch.randn(P, ps, Hkv, D, generator=g) if layout == "NHD"
+          else torch.randn(P, Hkv, ps, D, generator=g)).to(cache_dtype)
+    vc = (torch.randn(kc.shape, generator=g)).to(cache_dtype)
+    k = torch.randn(N, Hkv, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(N, Hkv, D, generator=g).to(torch.bfloat16)
+    slots = torch.randperm(P * ps, generator=g)[:N].to(torch.int64)
+    return kc, vc, k, v, slots
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_insert_then_decode_matches_dense_over_the_new_rows(layout):
+    # a sequence whose pages are listed in a page table; the new token goes to
+    # the slot after its last one; decoding the updated cache with L + 1 must
+    # equal dense attention over the old rows plus the inserted row
+    w = synth.WORKLOADS["tiny"].replace(kv_layout=layout, batch=1, fixed_seq_lens=(13,),
+                                        num_pages=8)
+    inp = synth.make_inputs(w, 11, "cpu", poison=False)
+    L, ps = 13, w.page_size
+    pt = inp["page_table_host"][0]
+    g = torch.Generator().manual_seed(12)
+    knew = torch.randn(1, 1, 128, generator=g).to(w.kv_dtype)
+    vnew = torch.randn(1, 1, 128, generator=g).to(w.kv_dtype)
+    slot = torch.tensor([int(pt[L // ps]) * ps + L % ps], dtype=torch.int64)
+    kc, vc = oracle.cache_insert(inp["k_cache"], inp["v_cache"], slot, knew, v=vnew, page_size=ps,
+                                 kv_layout=layout)
+    got = oracle.decode(inp["q"], kc, vc, inp["page_table"], torch.tensor([L + 1]), num_kv_heads=1,
+                        page_size=ps, kv_layout=layout)
+    K = torch.cat([dense.gather_rows(inp["k_cache"], pt, L, ps, 0, layout), dense.to_f64(knew[0])])
+    V = torch.cat([dense.gather_rows(inp["v_cache"], pt, L, ps, 0, layout), dense.to_f64(vnew[0])])
+    q = dense.to_f64(inp["q"]).reshape(-1, 128)
+    for h in range(q.shape[0]):
+        ref = dense.attention(q[h], K, V, torch.ones(L + 1, dtype=torch.bool), 128 ** -0.5)
+        assert torch.allclose(got.reshape(-1, 128)[h], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_insert_writes_exactly_the_mapped_rows(layout):
+    kc, vc, k, v, slots = _insert_case(layout)
+    slots[1] = -1                       # padding
+    slots[3] = kc.shape[0] * 4 + 2      # past the pool: ignored too
+    nk, nv = oracle.cache_insert(kc, vc, slots, k, v=v, page_size=4, kv_layout=layout)
+    # expected: a gather/scatter built with torch indexing over (page, offset)
+    ek, ev = kc.clone(), vc.clone()
+    for i, s in enumerate(slots.tolist()):
+        if s < 0 or s >= kc.shape[0] * 4:
+            continue
+        if layout == "NHD":
+            ek[s // 4, s % 4], ev[s // 4, s % 4] = k[i], v[i]
+        else:
+            ek[s // 4, :, s % 4], ev[s // 4, :, s % 4] = k[i], v[i]
+    assert torch.equal(nk.view(torch.int16), ek.view(torch.int16))
+    assert torch.equal(nv.view(torch.int16), ev.view(torch.int16))
+
+
+def test_insert_nhd_and_hnd_hold_the_same_rows():
+    kn, vn, k, v, slots = _insert_case("NHD")
+    kh, vh = kn.permute(0, 2, 1, 3).contiguous(), vn.permute(0, 2, 1, 3).contiguous()
+    a = oracle.cache_insert(kn, vn, slots, k, v=v, page_size=4, kv_layout="NHD")
+    b = oracle.cache_insert(kh, vh, slots, k, v=v, page_size=4, kv_layout="HND")
+    assert torch.equal(a[0].permute(0, 2, 1, 3).view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1].permute(0, 2, 1, 3).view(torch.int16), b[1].view(torch.int16))
+
+
+def test_insert_fp8_stores_the_scaled_value_rounded_to_e4m3():
+    kc, vc, k, v, slots = _insert_case("NHD", cache_dtype=torch.float8_e4m3fn)
+    s_inv = 20.0
+    nk, nv = oracle.cache_insert(kc, vc, slots, k, v=v, page_size=4, kv_layout="NHD",
+                                 cache_scale_inv=s_inv)
+    for i, s in enumerate(slots.tolist()):
+        # torch: binary32 product, then its RNE cast (all products are < 448 here)
+        want_k = (k[i].float() * torch.tensor(s_inv, dtype=torch.float32)).to(torch.float8_e4m3fn)
+        want_v = (v[i].float() * torch.tensor(s_inv, dtype=torch.float32)).to(torch.float8_e4m3fn)
+        assert torch.equal(nk[s // 4, s % 4].view(torch.uint8), want_k.view(torch.uint8))
+        assert torch.equal(nv[s // 4, s % 4].view(torch.uint8), want_v.view(torch.uint8))
+
+
+def test_insert_latent_row_is_the_concatenation():
+    # the latent cache row [kv_c_normed | k_pe]: one KV head, no V cache
+    g = torch.Generator().manual_seed(8)
+    cache = torch.randn(6, 4, 1, 576, generator=g).to(torch.bfloat16)
+    kvc = torch.randn(3, 1, 512, generator=g).to(torch.bfloat16)
+    kpe = torch.randn(3, 1, 64, generator=g).to(torch.bfloat16)
+    slots = torch.tensor([5, 17, 2], dtype=torch.int64)
+    nc, _ = oracle.cache_insert(cache, None, slots, kvc, k_rope=kpe, page_size=4)
+    for i, s in enumerate(slots.tolist()):
+        assert torch.equal(nc[s // 4, s % 4, 0].view(torch.int16),
+                           torch.cat([kvc[i, 0], kpe[i, 0]]).view(torch.int16))
+    untouched = torch.ones(24, dtype=torch.bool)
+    untouched[slots] = False
+    assert torch.equal(nc.view(24, 576)[untouched].view(torch.int16),
+                       cache.view(24, 576)[untouched].view(torch.int16))
