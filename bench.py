@@ -29,6 +29,13 @@ row serves as K and V and counts once.
 
 times the cache write side instead (pkv_cache_insert: new tokens' rows into
 their slots): value = bytes read + bytes written per call / wall time.
+
+    python bench.py --workload latent_absorb | latent_up_proj
+
+times the latent-attention projections around the decode (pkv_head_matmul:
+BMM1 with W_UK_T, the up-projection with W_UV) for the latent workload's 32
+decode tokens and 64 heads; value = bytes read + written / wall time (the
+weights dominate).
 """
 from __future__ import annotations
 
@@ -105,6 +112,8 @@ def main():
 
     if args.workload in INSERT_WORKLOADS:
         return bench_insert(args)
+    if args.workload in PROJ_WORKLOADS:
+        return bench_proj(args)
 
     import paged_kv_attention_pages_amd as pkv
     from paged_kv_attention_pages_amd import synth
@@ -236,6 +245,65 @@ INSERT_WORKLOADS = {
     "insert_latent_decode": dict(N=32, Hkv=1, Dk=576, Dlo=512, Dv=0, ps=64, layout="NHD",
                                  cache=torch.bfloat16, Hq=64),
 }
+
+
+PROJ_WORKLOADS = {
+    "latent_absorb": dict(M=32, H=64, K=128, N=512),
+    "latent_up_proj": dict(M=32, H=64, K=512, N=128),
+}
+
+
+def bench_proj(args):
+    import paged_kv_attention_pages_amd as pkv
+    cfg = PROJ_WORKLOADS[args.workload]
+    M, H, K, N = cfg["M"], cfg["H"], cfg["K"], cfg["N"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev).manual_seed(1)
+    x = torch.randn(M, H, K, generator=g, device=dev).to(torch.bfloat16)
+    # weights rotate through replicas totalling >= 1 GB (read from HBM each call)
+    wb = H * K * N * 2
+    n_rep = min(128, max(1, math.ceil(1.0e9 / wb)))
+    ws = [(torch.randn(H, K, N, generator=g, device=dev) / math.sqrt(K)).to(torch.bfloat16)
+          for _ in range(n_rep)]
+    y = torch.empty(M, H, N, dtype=torch.bfloat16, device=dev)
+    nbytes = wb + M * H * (K + N) * 2
+    K_, W_ = args.steps, args.warmup
+    for i in range(W_):
+        pkv.head_matmul(x, ws[i % n_rep], y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K_):
+        pkv.head_matmul(x, ws[i % n_rep], y)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K_
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K_)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        pkv.head_matmul(x, ws[i % n_rep], y)
+        b.record()
+    torch.cuda.synchronize()
+    kern_ms = statistics.fmean(a.elapsed_time(b) for a, b in ev)
+    value = nbytes / (ms * 1e-3) / 1e9
+    flops = 2.0 * M * H * K * N
+    print(f"[bench] {args.workload}: {ms * 1e3:.2f} us/call wall, evented {kern_ms * 1e3:.2f} us, "
+          f"{value:.0f} GB/s", file=sys.stderr, flush=True)
+    rec = {
+        "metric": "latent projection GB/s (bytes read + written) + us/call",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K_, "warmup": W_,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "us_per_call": round(ms * 1e3, 2),
+        "config": {"workload": args.workload, "tokens": M, "heads": H, "k": K, "n": N,
+                   "bytes_per_call": nbytes, "flops_per_call": flops, "weight_replicas": n_rep},
+        "roofline": {"kernel": "head matmul", "bound": "hbm",
+                     "achieved": round(nbytes / (kern_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": nbytes,
+                     "launch_us_mean": round(kern_ms * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
 
 
 def bench_insert(args):

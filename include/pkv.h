@@ -264,6 +264,26 @@ pkv_status pkv_cache_insert(const void* k_src, const void* k_rope_src, const voi
                             const void* q_lo, const void* q_hi, void* q_out, void* stream,
                             const pkv_insert_dims* dims);
 
+/* ---- the latent-attention projections around the decode ------------- */
+
+/* Per-head product y[m, h, 0:N] = x[m, h, 0:K] . W[h] for m < M, h < H (vLLM
+ * Kimi-K3 MLA page, `_attention` decode branch: BMM1, which absorbs q_nope
+ * into the latent space with W_UK_T [H, qk_nope_head_dim, kv_lora_rank]
+ * before the latent decode, and `_v_up_proj`, which takes the
+ * kv_lora_rank-wide decode output back to v_head_dim with W_UV [H,
+ * kv_lora_rank, v_head_dim]).
+ *   x: element (m, h, k) at x + m * x_stride_m + h * x_stride_h + k
+ *      (strides in elements, multiples of 8: e.g. the q_nope part of q);
+ *   w: [H, K, N] contiguous (the page's layout);
+ *   y: element (m, h, n) at y + m * y_stride_m + h * y_stride_h + n
+ *      (strides multiples of 4).
+ * dtype PKV_BF16 or PKV_F16 for x, w and y; fp32 accumulation, one rounding
+ * (nearest even) to the output.  K must be a multiple of 32 and N of 64;
+ * pointers 16-byte aligned.  One launch on `stream`. */
+pkv_status pkv_head_matmul(const void* x, int64_t x_stride_m, int64_t x_stride_h, const void* w,
+                           void* y, int64_t y_stride_m, int64_t y_stride_h, int M, int H, int K,
+                           int N, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

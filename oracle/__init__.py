@@ -196,3 +196,46 @@ def cache_insert(k_cache, v_cache, slot_mapping, k, k_rope=None, v=None, *, page
     if rc < 0:
         raise ValueError("oracle: malformed insert sizes")
     return kc, vc
+
+
+def head_matmul(x, w):
+    """y[m, h] = x[m, h] . w[h] in fp64 (torch's matmul on the decoded values).
+
+    The per-head products of the vLLM Kimi-K3 MLA page around its latent
+    decode: BMM1 with W_UK_T and `_v_up_proj` with W_UV.
+    """
+    xd = x.detach().to("cpu", torch.float64)
+    wd = w.detach().to("cpu", torch.float64)
+    return torch.matmul(xd.transpose(0, 1), wd).transpose(0, 1).contiguous()
+
+
+def mla_materialised(q_nope, q_pe, kv_cache, page_table, seq_lens, w_uk_t, w_uv, *, page_size,
+                     kv_lora_rank=512, softmax_scale):
+    """Multi-head attention with the keys and values materialised from the latent
+    cache, in fp64 -- the form the absorbed decode must equal (vLLM Kimi-K3 MLA
+    page: K_nope = kv_c . W_UK, K = [K_nope | k_pe], V = kv_c . W_UV).
+
+    q_nope [B, H, P], q_pe [B, H, R], kv_cache [pages, page_size, 1, kv_lora_rank + R]
+    (rows [kv_c | k_pe]), w_uk_t [H, P, L], w_uv [H, L, V].  Returns [B, H, V].
+    """
+    B, H, _ = q_nope.shape
+    L = kv_lora_rank
+    cache = kv_cache.detach().to("cpu", torch.float64).reshape(-1, kv_cache.shape[-1])
+    wuk = w_uk_t.detach().to("cpu", torch.float64)          # [H, P, L]
+    wuv = w_uv.detach().to("cpu", torch.float64)            # [H, L, V]
+    qn = q_nope.detach().to("cpu", torch.float64)
+    qp = q_pe.detach().to("cpu", torch.float64)
+    out = torch.zeros(B, H, wuv.shape[-1], dtype=torch.float64)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n == 0:
+            continue
+        t = torch.arange(n)
+        rows = cache[page_table[b].to(torch.int64)[t // page_size] * page_size + t % page_size]
+        kv_c, k_pe = rows[:, :L], rows[:, L:]
+        for h in range(H):
+            k_nope = kv_c @ wuk[h].T                        # [n, P]
+            v = kv_c @ wuv[h]                               # [n, V]
+            logits = softmax_scale * (k_nope @ qn[b, h] + k_pe @ qp[b, h])
+            out[b, h] = torch.softmax(logits, dim=0) @ v
+    return out

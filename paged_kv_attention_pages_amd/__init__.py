@@ -110,6 +110,11 @@ def lib():
                 L.pkv_validate_inputs.restype = ctypes.c_int
                 L.pkv_validate_inputs.argtypes = [_vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                   ctypes.c_int, _vp, ctypes.POINTER(Dims)]
+                L.pkv_head_matmul.restype = ctypes.c_int
+                L.pkv_head_matmul.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, _vp, _vp,
+                                              ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, _vp]
                 L.pkv_cache_insert.restype = ctypes.c_int
                 L.pkv_cache_insert.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                                _vp, _vp, _vp, _vp, ctypes.POINTER(InsertDims)]
@@ -391,3 +396,38 @@ def cache_insert(k_cache, v_cache, slot_mapping, k, k_rope=None, v=None, *, page
                                     ctypes.byref(d))
     _check(st)
     return k_cache
+
+
+def head_matmul(x, w, y=None, *, stream=None):
+    """Per-head product y[m, h] = x[m, h] . w[h] (one launch).
+
+    x [M, H, K] (any strides with a contiguous last dim, e.g. the q_nope
+    slice of q), w [H, K, N] contiguous (the latent-attention weights W_UK_T
+    or W_UV in their stored layout), y [M, H, N] (allocated when None; may
+    be a strided view).  bf16 or f16 throughout.  Returns y.
+    """
+    if x.device.type != "cuda":
+        raise PkvError(1, "head_matmul runs on the GPU only")
+    if x.dim() != 3 or w.dim() != 3 or x.shape[1] != w.shape[0] or x.shape[2] != w.shape[1]:
+        raise PkvError(1, f"x must be [M, H, K] and w [H, K, N]; got {tuple(x.shape)} and "
+                          f"{tuple(w.shape)}")
+    if x.dtype not in (torch.float16, torch.bfloat16) or w.dtype != x.dtype:
+        raise PkvError(1, "x and w must share dtype float16 or bfloat16")
+    if not w.is_contiguous() or x.stride(2) != 1:
+        raise PkvError(1, "w must be contiguous and x's last dim contiguous")
+    M, H, K = x.shape
+    N = w.shape[2]
+    if y is None:
+        y = torch.empty((M, H, N), dtype=x.dtype, device=x.device)
+    if tuple(y.shape) != (M, H, N) or y.dtype != x.dtype or y.stride(2) != 1:
+        raise PkvError(1, f"y must be [{M}, {H}, {N}] of x's dtype with a contiguous last dim")
+    for t in (w, y):
+        if t.device != x.device:
+            raise PkvError(1, "x, w and y must be on one device")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        st = lib().pkv_head_matmul(_ptr(x), x.stride(0), x.stride(1), _ptr(w), _ptr(y), y.stride(0),
+                                   y.stride(1), M, H, K, N, _DTYPE[x.dtype], ctypes.c_void_p(stream))
+    _check(st)
+    return y

@@ -515,4 +515,44 @@ pkv_status pkv_cache_insert(const void* k_src, const void* k_rope_src, const voi
   return PKV_OK;
 }
 
+pkv_status pkv_head_matmul(const void* x, int64_t xs_m, int64_t xs_h, const void* w, void* y,
+                           int64_t ys_m, int64_t ys_h, int M, int H, int K, int N, int dtype,
+                           void* stream) {
+  if (M < 0 || H < 1 || K < 32 || K % 32 || N < 64 || N % 64)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "head_matmul needs M >= 0, H >= 1, K a multiple of 32 "
+                                          "and N a multiple of 64 (got M %d, H %d, K %d, N %d)",
+                M, H, K, N);
+  if (dtype != PKV_F16 && dtype != PKV_BF16)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "head_matmul dtype must be float16 or bfloat16; got %d",
+                dtype);
+  if (xs_m % 8 || xs_h % 8 || ys_m % 4 || ys_h % 4 || xs_m < 0 || xs_h < 0 || ys_m < 0 || ys_h < 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "head_matmul strides must be non-negative, x's multiples "
+                                          "of 8 and y's of 4 elements");
+  if (M == 0) {
+    g_err.clear();
+    return PKV_OK;
+  }
+  if (!x || !w || !y) return fail(PKV_ERR_INVALID_ARGUMENT, "x, w and y must not be NULL");
+  if (misaligned(x, 16) || misaligned(w, 16) || misaligned(y, 16))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "x, w and y must be 16-byte aligned");
+  if ((int64_t)H > 65535 || (int64_t)N / 64 > 65535)
+    return fail(PKV_ERR_UNSUPPORTED, "head_matmul: H and N / 64 must be <= 65535");
+  pkv::HeadMatmulParams p{};
+  p.x = x;
+  p.w = w;
+  p.y = y;
+  p.xs_m = xs_m;
+  p.xs_h = xs_h;
+  p.ys_m = ys_m;
+  p.ys_h = ys_h;
+  p.M = M;
+  p.H = H;
+  p.K = K;
+  p.N = N;
+  const hipError_t e = pkv::launch_head_matmul(dtype, p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "head_matmul launch failed: %s", hipGetErrorString(e));
+  g_err.clear();
+  return PKV_OK;
+}
+
 }  // extern "C"

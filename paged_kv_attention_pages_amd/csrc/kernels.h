@@ -35,6 +35,16 @@ struct InsertParams {
 };
 hipError_t launch_cache_insert(int src_dtype, int cache_dtype, const InsertParams& p, hipStream_t s);
 
+// Per-head products around the latent decode: y[m, h] = x[m, h] . W[h].
+struct HeadMatmulParams {
+  const void* x;              // element (m, h, k) at m * xs_m + h * xs_h + k
+  const void* w;              // [H, K, N] row-major
+  void* y;                    // element (m, h, n) at m * ys_m + h * ys_h + n
+  int64_t xs_m, xs_h, ys_m, ys_h;
+  int M, H, K, N;
+};
+hipError_t launch_head_matmul(int dtype, const HeadMatmulParams& p, hipStream_t s);
+
 // Log-sum-exp merge of the split partials of every sequence that needed
 // more than one split (zeros for sequences with nothing visible).
 hipError_t launch_combine(int q_dtype, const Params& p, hipStream_t s);

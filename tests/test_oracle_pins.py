@@ -570,3 +570,50 @@ def test_insert_latent_row_is_the_concatenation():
     untouched[slots] = False
     assert torch.equal(nc.view(24, 576)[untouched].view(torch.int16),
                        cache.view(24, 576)[untouched].view(torch.int16))
+
+
+# ---------------------------------------------------------------- latent projections
+
+def test_absorbed_decode_equals_materialised_attention():
+    # the latent (absorbed) decode -- q_nope . W_UK_T, attention over the
+    # latent rows, then . W_UV -- against multi-head attention with K and V
+    # materialised from the latent cache (random weights)
+    w = synth.WORKLOADS["mla"].replace(batch=3, num_q_heads=4, seq_len_range=(5, 150))
+    inp = synth.make_inputs(w, 21, "cpu", poison=False)
+    g = torch.Generator().manual_seed(22)
+    B, H, P, R, L, V = 3, 4, 128, 64, 512, 128
+    q_nope = torch.randn(B, H, P, generator=g).to(torch.bfloat16)
+    q_pe = inp["q"].reshape(B, H, 576)[:, :, L:].contiguous()
+    w_uk_t = (torch.randn(H, P, L, generator=g) / math.sqrt(P)).to(torch.bfloat16)
+    w_uv = (torch.randn(H, L, V, generator=g) / math.sqrt(L)).to(torch.bfloat16)
+    scale = 192 ** -0.5
+    want = oracle.mla_materialised(q_nope, q_pe, inp["k_cache"], inp["page_table"], inp["seq_lens"],
+                                   w_uk_t, w_uv, page_size=w.page_size, softmax_scale=scale)
+    # the absorbed form, in fp64 throughout: ql_nope = q_nope . W_UK_T, one
+    # shared latent key/value row per token, softmax, then . W_UV
+    ql = oracle.head_matmul(q_nope, w_uk_t)
+    cache = inp["k_cache"].to(torch.float64).reshape(-1, 576)
+    lat = torch.zeros(B, H, L, dtype=torch.float64)
+    for b in range(B):
+        n = int(inp["seq_lens"][b])
+        t = torch.arange(n)
+        rows = cache[inp["page_table"][b].to(torch.int64)[t // w.page_size] * w.page_size + t % w.page_size]
+        for h in range(H):
+            q = torch.cat([ql[b, h], q_pe[b, h].to(torch.float64)])
+            lat[b, h] = torch.softmax(scale * (rows @ q), dim=0) @ rows[:, :L]
+    got = oracle.head_matmul(lat, w_uv)
+    assert torch.allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_head_matmul_brute_force():
+    # every output element as an explicit sum over k, on a tiny case
+    g = torch.Generator().manual_seed(23)
+    x = torch.randn(3, 2, 8, generator=g).to(torch.bfloat16)
+    w = torch.randn(2, 8, 5, generator=g).to(torch.bfloat16)
+    y = oracle.head_matmul(x, w)
+    xs, ws = x.double().tolist(), w.double().tolist()
+    for m in range(3):
+        for h in range(2):
+            for n in range(5):
+                want = math.fsum(xs[m][h][k] * ws[h][k][n] for k in range(8))
+                assert abs(y[m, h, n].item() - want) <= 1e-12
