@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 
 typedef enum {
   PKV_OK = 0,
@@ -142,6 +142,13 @@ typedef struct pkv_options {
    * 2 = split kernel (one launch).  Other plans always use the combine
    * kernel.  (ABI version 3.) */
   int32_t merge_mode;
+  /* xqa page, `output` ("dtype of q or of the KV cache") and `rcp_out_scale`
+   * ("reciprocal of the output scale"): nonzero out_fp8 writes the output as
+   * E4M3 bytes (an fp8 KV cache only) holding round(out * rcp_out_scale) --
+   * binary32 product, nearest even, magnitudes past 448 saturated;
+   * rcp_out_scale 0 means 1.  (ABI version 4.) */
+  int32_t out_fp8;
+  float rcp_out_scale;
 } pkv_options;
 
 /* The plan a decode call would use (pkv_query_plan). */

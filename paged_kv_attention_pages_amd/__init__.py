@@ -53,7 +53,8 @@ class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("split_pages", ctypes.c_int32),
                 ("num_cus", ctypes.c_int32), ("target_ctas", ctypes.c_int32),
                 ("split_event", ctypes.c_void_p), ("q_scale_dev", ctypes.c_void_p),
-                ("kv_scale_dev", ctypes.c_void_p), ("merge_mode", ctypes.c_int32)]
+                ("kv_scale_dev", ctypes.c_void_p), ("merge_mode", ctypes.c_int32),
+                ("out_fp8", ctypes.c_int32), ("rcp_out_scale", ctypes.c_float)]
 
 
 class InsertDims(ctypes.Structure):
@@ -150,9 +151,10 @@ def _dims(q, k_cache, page_table, head_dim_v, q_seq_len, workspace_bytes=0) -> D
 
 
 def _options(path=None, split_pages=0, num_cus=0, target_ctas=0, split_event=None,
-             q_scale_dev=None, kv_scale_dev=None, single_launch=None):
+             q_scale_dev=None, kv_scale_dev=None, single_launch=None, out_fp8=False,
+             rcp_out_scale=1.0):
     if not (path or split_pages or num_cus or target_ctas or split_event or q_scale_dev
-            or kv_scale_dev or single_launch is not None):
+            or kv_scale_dev or single_launch is not None or out_fp8):
         return None
     o = Options()
     o.path = {None: 0, "auto": 0, "valu": 1, "mfma": 2, "mfma_mla": 3}.get(path, path)
@@ -160,6 +162,8 @@ def _options(path=None, split_pages=0, num_cus=0, target_ctas=0, split_event=Non
     o.split_event = split_event
     o.q_scale_dev, o.kv_scale_dev = q_scale_dev, kv_scale_dev
     o.merge_mode = 0 if single_launch is None else 2 if single_launch else 1
+    o.out_fp8 = 1 if out_fp8 else 0
+    o.rcp_out_scale = float(rcp_out_scale)
     return o
 
 
@@ -232,9 +236,12 @@ def _shape_checks(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_head
     if seq_lens.dtype not in (torch.int32, torch.uint32) or seq_lens.numel() != B:
         raise PkvError(1, f"seq_lens must be uint32 (or int32) [batch] or [batch, 1], got "
                           f"{seq_lens.dtype} {tuple(seq_lens.shape)}")
-    if output.dtype != q.dtype or output.numel() != B * q_seq_len * Hq * head_dim_v:
-        raise PkvError(1, f"output must have q's dtype and batch x q_seq_len x num_q_heads x "
-                          f"head_dim_v elements, got {output.dtype} {tuple(output.shape)}")
+    out_ok = output.dtype == q.dtype or (output.dtype in (torch.float8_e4m3fn, torch.uint8)
+                                         and k_cache.dtype in (torch.float8_e4m3fn, torch.uint8))
+    if not out_ok or output.numel() != B * q_seq_len * Hq * head_dim_v:
+        raise PkvError(1, f"output must have q's dtype (or the fp8 cache's) and batch x q_seq_len "
+                          f"x num_q_heads x head_dim_v elements, got {output.dtype} "
+                          f"{tuple(output.shape)}")
     if mask is not None and q_seq_len > 1:
         want = (B, q_seq_len, ((q_seq_len + 31) // 32) * 2)
         if mask.dtype not in (torch.uint16, torch.int16) or tuple(mask.shape) != want:
@@ -252,7 +259,7 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
                 num_kv_heads, page_size, sinks=None, q_scale=1.0, kv_scale=1.0,
                 sliding_win_size=0, kv_layout="NHD", q_seq_len=1, mask=None, head_dim_v=None,
                 path=None, split_pages=0, target_ctas=0, stream=None, split_event=None,
-                single_launch=None):
+                single_launch=None, rcp_out_scale=1.0):
     """Paged-KV decode attention, written in place into ``output``.
 
     q [B, q_seq_len, Hq, Dqk] (or [B, Hq, Dqk], or the xqa page's beam-1
@@ -265,7 +272,9 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
     once) is recorded after the split-KV kernel (before the combine kernel,
     when the plan has one).  ``single_launch`` (None: the planner's choice)
     makes the matrix-core stream-K plan merge cut units in the split kernel
-    (True) or in a second kernel (False).  Returns ``output``.
+    (True) or in a second kernel (False).  A float8_e4m3fn ``output`` (fp8
+    caches only, as the xqa page allows the cache's dtype) receives
+    round(out * rcp_out_scale).  Returns ``output``.
     """
     if head_dim_v is None:
         head_dim_v = output.shape[-1]
@@ -280,8 +289,9 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
     ev = None if split_event is None else split_event.cuda_event
     q_scale, q_scale_dev = _scale_arg(q_scale, "q_scale", q.device)
     kv_scale, kv_scale_dev = _scale_arg(kv_scale, "kv_scale", q.device)
+    out_fp8 = output.dtype in (torch.float8_e4m3fn, torch.uint8)
     opts = _options(path, split_pages, 0, target_ctas, ev, q_scale_dev, kv_scale_dev,
-                    single_launch)
+                    single_launch, out_fp8, rcp_out_scale)
     d = _dims(q, k_cache, page_table, head_dim_v, q_seq_len)
     if workspace_buffer is None:
         info = PlanInfo()

@@ -251,6 +251,13 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
     return fail(PKV_ERR_INVALID_ARGUMENT, "q_scale and kv_scale must be finite");
   if (opts && (misaligned(opts->q_scale_dev, 4) || misaligned(opts->kv_scale_dev, 4)))
     return fail(PKV_ERR_INVALID_ARGUMENT, "device q_scale / kv_scale must be 4-byte aligned");
+  const bool out_fp8 = opts && opts->out_fp8;
+  const float rcp_out = (opts && opts->rcp_out_scale != 0.f) ? opts->rcp_out_scale : 1.f;
+  if (out_fp8 && d->kv_dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "an float8_e4m3fn output needs an float8_e4m3fn KV cache "
+                                          "(the output dtype is q's or the cache's)");
+  if (!std::isfinite(rcp_out) || rcp_out <= 0.f)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "rcp_out_scale must be finite and positive");
   if (pl.ws_bytes > 0) {
     if (workspace == nullptr)
       return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "workspace is NULL; %zu bytes needed", pl.ws_bytes);
@@ -307,6 +314,8 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
   p.kv_scale = kv_scale;
   p.qk_unit = (float)(1.4426950408889634 / std::sqrt((double)Dk));
   p.fused = pl.fused ? 1 : 0;
+  p.out_fp8 = out_fp8 ? 1 : 0;
+  p.rcp_out_scale = rcp_out;
   p.ws_cnt = pl.fused ? (unsigned long long*)((char*)workspace + pl.ws_cnt_off) : nullptr;
   p.gen = pl.fused ? g_gen.fetch_add(1, std::memory_order_relaxed) + 1u : 0u;
   if (p.B > 65535 || Hkv > 65535)

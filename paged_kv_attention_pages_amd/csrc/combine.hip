@@ -27,9 +27,9 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
   const SeqGeom sg = seq_geom(p, b);
   if (sg.nsplits == 1) return;
   const int lane = threadIdx.x;
-  uint16_t* o = (uint16_t*)p.out + q_row_offset(p, b, kvh, r) * p.Dv;
+  const int64_t ob = q_row_offset(p, b, kvh, r) * p.Dv;
   if (sg.nsplits == 0) {
-    for (int d = lane * 4; d < p.Dv; d += 256) *(uint2*)(o + d) = make_uint2(0u, 0u);
+    for (int d = lane * 4; d < p.Dv; d += 256) store_out4<QT>(p, ob + d, 0.f, 0.f, 0.f, 0.f);
     return;
   }
   const int64_t base = ((int64_t)b * p.Hkv + kvh) * p.max_splits * p.R + r;  // split stride R
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
       const float4 v = *(const float4*)(p.ws_o + prow * p.Dv + d);
       a.x += w * v.x; a.y += w * v.y; a.z += w * v.z; a.w += w * v.w;
     }
-    *(uint2*)(o + d) = make_uint2(pack2<QT>(a.x * inv, a.y * inv), pack2<QT>(a.z * inv, a.w * inv));
+    store_out4<QT>(p, ob + d, a.x * inv, a.y * inv, a.z * inv, a.w * inv);
   }
 }
 
@@ -78,9 +78,9 @@ __global__ __launch_bounds__(256) void combine_sk_kernel(Params p) {
   const int W = sk_waves_eff(S.T, p.sk_waves);
   int pre, n;
   sk_seq_of(S, b, &pre, &n);
-  uint16_t* o = (uint16_t*)p.out + q_row_offset(p, b, kvh, r) * p.Dv;
+  const int64_t ob = q_row_offset(p, b, kvh, r) * p.Dv;
   if (n == 0) {
-    for (int d = lane; d < p.Dv; d += 64) o[d] = 0;
+    for (int d = lane; d < p.Dv; d += 64) store_out1<QT>(p, ob + d, 0.f);
     return;
   }
   const int64_t us = (int64_t)pre * p.Hkv + (int64_t)kvh * n, ue = us + n;
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void combine_sk_kernel(Params p) {
   const float inv = den > 0.f ? p.out_scale / den : 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k)
-    if (k < per_lane) o[lane + 64 * k] = (uint16_t)(pack2<QT>(acc[k] * inv, 0.f) & 0xffffu);
+    if (k < per_lane) store_out1<QT>(p, ob + lane + 64 * k, acc[k] * inv);
 }
 
 hipError_t launch_combine(int q_dtype, const Params& p, hipStream_t s) {

@@ -45,6 +45,10 @@ struct Params {
   unsigned long long* ws_cnt; // [B * Hkv]
   unsigned gen;
   int fused;
+  // E4M3 output (xqa `output` in the KV dtype): stored value =
+  // round(out * rcp_out_scale); 0 = 16-bit output in q's dtype
+  int out_fp8;
+  float rcp_out_scale;
 };
 
 // Scales from device memory when the call passed them there: every kernel
@@ -291,6 +295,35 @@ __device__ __forceinline__ float2 unpack2(uint32_t w) {
     const f16x2 h = __builtin_bit_cast(f16x2, w);
     return make_float2((float)h[0], (float)h[1]);
   }
+}
+
+// ------------------------------------------------------------ output stores
+// Four consecutive output elements starting at element e (e % 4 == 0): in
+// q's dtype, or as E4M3 bytes of value * rcp_out_scale (binary32 product,
+// clamped to +-448 with NaN kept, then v_cvt_pk_fp8_f32's round to nearest
+// even).
+__device__ __forceinline__ float sat448(float x) { return x != x ? x : fminf(fmaxf(x, -448.f), 448.f); }
+
+template <int QT>
+__device__ __forceinline__ void store_out4(const Params& p, int64_t e, float a, float b, float c, float d) {
+  if (p.out_fp8) {
+    const float s = p.rcp_out_scale;
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a * s), sat448(b * s), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c * s), sat448(d * s), w, true);
+    *(uint32_t*)((uint8_t*)p.out + e) = w;
+  } else {
+    *(uint2*)((uint16_t*)p.out + e) = make_uint2(pack2<QT>(a, b), pack2<QT>(c, d));
+  }
+}
+
+// One output element.
+template <int QT>
+__device__ __forceinline__ void store_out1(const Params& p, int64_t e, float a) {
+  if (p.out_fp8)
+    ((uint8_t*)p.out)[e] =
+        (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(sat448(a * p.rcp_out_scale), 0.f, 0, false) & 0xff);
+  else
+    ((uint16_t*)p.out)[e] = (uint16_t)(pack2<QT>(a, 0.f) & 0xffffu);
 }
 
 // Softmax reference slack (log2 units): a kernel moves its running

@@ -274,14 +274,13 @@ __device__ __forceinline__ void finish_unit(const Params& p, const Unit<KT, D>& 
       den = l * num + exp2f(sk - Mf);
     }
     const float inv = den > 0.f ? p.out_scale * num / den : 0.f;
-    uint16_t* o = (uint16_t*)p.out + q_row_offset(p, U.b, U.kvh, n) * p.Dv;
+    const int64_t ob = q_row_offset(p, U.b, U.kvh, n) * p.Dv;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < DT; j += 4)
-        *(uint2*)(o + DT * (4 * g + i) + j) =
-            make_uint2(pack2<QT>(A.o[j][i] * inv, A.o[j + 1][i] * inv),
-                       pack2<QT>(A.o[j + 2][i] * inv, A.o[j + 3][i] * inv));
+        store_out4<QT>(p, ob + DT * (4 * g + i) + j, A.o[j][i] * inv, A.o[j + 1][i] * inv,
+                       A.o[j + 2][i] * inv, A.o[j + 3][i] * inv);
   } else {
     float* o = p.ws_o + prow * p.Dv;
 #pragma unroll
@@ -428,14 +427,13 @@ __device__ __forceinline__ void merge_unit(const Params& p, const Pending& u) {
       den = den * num + exp2f(sk - Mf);
     }
     const float inv = den > 0.f ? p.out_scale * num / den : 0.f;
-    uint16_t* o = (uint16_t*)p.out + q_row_offset(p, u.b, u.kvh, n) * p.Dv;
+    const int64_t ob = q_row_offset(p, u.b, u.kvh, n) * p.Dv;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < DT; j += 4)
-        *(uint2*)(o + DT * (4 * g + i) + j) =
-            make_uint2(pack2<QT>(acc[j][i] * inv, acc[j + 1][i] * inv),
-                       pack2<QT>(acc[j + 2][i] * inv, acc[j + 3][i] * inv));
+        store_out4<QT>(p, ob + DT * (4 * g + i) + j, acc[j][i] * inv, acc[j + 1][i] * inv,
+                       acc[j + 2][i] * inv, acc[j + 3][i] * inv);
   }
   if (lane == 0)
     __hip_atomic_store(p.ws_cnt + (u.b * p.Hkv + u.kvh), (unsigned long long)p.gen << 32,
@@ -452,8 +450,8 @@ __device__ __forceinline__ void zero_empty_units(const Params& p, const SkSched&
     if (n != 0) continue;
     for (int kvh = 0; kvh < p.Hkv; ++kvh)
       for (int r = 0; r < p.R; ++r) {
-        uint16_t* o = (uint16_t*)p.out + q_row_offset(p, b, kvh, r) * p.Dv;
-        for (int d = 4 * lane; d < p.Dv; d += 256) *(uint2*)(o + d) = make_uint2(0u, 0u);
+        const int64_t ob = q_row_offset(p, b, kvh, r) * p.Dv;
+        for (int d = 4 * lane; d < p.Dv; d += 256) store_out4<kBF16>(p, ob + d, 0.f, 0.f, 0.f, 0.f);
       }
   }
 }

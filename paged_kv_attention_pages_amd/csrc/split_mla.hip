@@ -437,11 +437,10 @@ __device__ __forceinline__ void finish_piece(const Params& p, const Piece& P, Ac
       den = l * num + exp2f(sk - Mf);
     }
     const float inv = den > 0.f ? p.out_scale * num / den : 0.f;
-    uint16_t* o = (uint16_t*)p.out + q_row_offset(p, P.b, P.kvh, row) * kDv + kPvHalf * h + 4 * g;
+    const int64_t ob = q_row_offset(p, P.b, P.kvh, row) * kDv + kPvHalf * h + 4 * g;
 #pragma unroll
     for (int m = 0; m < 16; ++m)
-      *(uint2*)(o + 16 * m) = make_uint2(pack2<QT>(A.o[m][0] * inv, A.o[m][1] * inv),
-                                         pack2<QT>(A.o[m][2] * inv, A.o[m][3] * inv));
+      store_out4<QT>(p, ob + 16 * m, A.o[m][0] * inv, A.o[m][1] * inv, A.o[m][2] * inv, A.o[m][3] * inv);
   } else {
     float* o = p.ws_o + (prow0 + row) * kDv + kPvHalf * h + 4 * g;
 #pragma unroll

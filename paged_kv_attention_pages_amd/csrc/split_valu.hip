@@ -264,8 +264,8 @@ __global__ __launch_bounds__(256) void split_valu_kernel(Params p) {
         den = Ltot * num + exp2f(sk - Mf);
       }
       const float inv = den > 0.f ? p.out_scale * num / den : 0.f;
-      uint16_t* o = (uint16_t*)p.out + q_row_offset(p, b, kvh, r) * p.Dv + d;
-      *(uint2*)o = make_uint2(pack2<QT>(sum.x * inv, sum.y * inv), pack2<QT>(sum.z * inv, sum.w * inv));
+      store_out4<QT>(p, q_row_offset(p, b, kvh, r) * p.Dv + d, sum.x * inv, sum.y * inv, sum.z * inv,
+                     sum.w * inv);
     } else {
       const int64_t prow = (((int64_t)b * p.Hkv + kvh) * p.max_splits + split) * p.R + r;
       *(float4*)(p.ws_o + prow * p.Dv + d) = sum;

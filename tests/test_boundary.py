@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (pkv_\w+)", out))
     assert set(names) <= exported, set(names) - exported
-    assert pkv.lib().pkv_abi_version() == 3
+    assert pkv.lib().pkv_abi_version() == 4
 
 
 def test_struct_layouts_match_header(tmp_path):
@@ -53,7 +53,7 @@ int main(void) {
   printf("pkv_options %zu\\n", sizeof(pkv_options));
   printf("pkv_plan_info %zu\\n", sizeof(pkv_plan_info));
   F(pkv_dims, workspace_bytes) F(pkv_dims, kv_dtype) F(pkv_options, target_ctas) F(pkv_options, split_event) F(pkv_options, q_scale_dev) F(pkv_options, kv_scale_dev)
-  F(pkv_options, merge_mode)
+  F(pkv_options, merge_mode) F(pkv_options, rcp_out_scale)
   printf("pkv_insert_dims %zu\\n", sizeof(pkv_insert_dims));
   F(pkv_insert_dims, num_q_heads) F(pkv_insert_dims, cache_dtype)
   F(pkv_plan_info, workspace_bytes) F(pkv_plan_info, num_cus) F(pkv_plan_info, single_launch)
@@ -77,6 +77,7 @@ int main(void) {
     assert int(got["pkv_plan_info.workspace_bytes"]) == pkv.PlanInfo.workspace_bytes.offset
     assert int(got["pkv_plan_info.num_cus"]) == pkv.PlanInfo.num_cus.offset
     assert int(got["pkv_options.merge_mode"]) == pkv.Options.merge_mode.offset
+    assert int(got["pkv_options.rcp_out_scale"]) == pkv.Options.rcp_out_scale.offset
     assert int(got["pkv_insert_dims"]) == ctypes.sizeof(pkv.InsertDims)
     assert int(got["pkv_insert_dims.num_q_heads"]) == pkv.InsertDims.num_q_heads.offset
     assert int(got["pkv_insert_dims.cache_dtype"]) == pkv.InsertDims.cache_dtype.offset

@@ -681,3 +681,45 @@ def test_device_scale_arguments_checked():
             pkv.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"],
                             inp["seq_lens"], out, num_kv_heads=w.num_kv_heads,
                             page_size=w.page_size, kv_layout=w.kv_layout, q_scale=bad)
+
+
+# ---------------------------------------------------------------- fp8 output (rcp_out_scale)
+
+@pytest.mark.parametrize("rcp", [1.0, 6.0])
+@pytest.mark.parametrize("mode", ["sk", "grid", "valu", "one_launch"])
+def test_fp8_output_with_rcp_out_scale(mode, rcp):
+    # an fp8 cache may write an fp8 output holding round(out * rcp_out_scale);
+    # the decoded output / rcp is within the bound plus half an E4M3 step
+    w = SMALL["fp8"]
+    print(f"[case] fp8 output {mode} rcp={rcp}", flush=True)
+    inp = make(w, seed=95)
+    B = inp["q"].shape[0]
+    out = torch.full((B, w.q_seq_len, w.num_q_heads, w.head_dim_v), float("nan"),
+                     dtype=torch.float8_e4m3fn, device=DEV)
+    kw = {"sk": {}, "grid": {"split_pages": 3}, "valu": {"path": "valu"},
+          "one_launch": {"single_launch": True, "target_ctas": 7}}[mode]
+    pkv.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"], inp["seq_lens"],
+                    out, num_kv_heads=w.num_kv_heads, page_size=w.page_size, sinks=inp["sinks"],
+                    q_scale=w.q_scale, kv_scale=w.kv_scale, sliding_win_size=w.window,
+                    kv_layout=w.kv_layout, q_seq_len=w.q_seq_len, mask=inp["mask"],
+                    rcp_out_scale=rcp, **kw)
+    torch.cuda.synchronize()
+    ref = run_oracle(w, inp)
+    got = out.cpu().to(torch.float64) / rcp
+    assert not torch.isnan(got).any()
+    scaled = (ref * rcp).abs().clamp(min=2.0 ** -6)
+    half_step = 0.5 * torch.exp2(torch.floor(torch.log2(scaled)) - 3) / rcp   # 3 fraction bits
+    allowed = tol_for(w) + half_step
+    err = ((got - ref).abs() - allowed).max().item()
+    print(f"[parity] fp8-out/{mode}/rcp{rcp} worst margin {err:.3e}", flush=True)
+    assert err <= 0.0
+
+
+def test_fp8_output_needs_an_fp8_cache():
+    w = SMALL["gqa"]
+    inp = make(w, seed=96)
+    out = torch.empty((w.batch, 1, w.num_q_heads, 128), dtype=torch.float8_e4m3fn, device=DEV)
+    with pytest.raises(pkv.PkvError, match="dtype"):
+        pkv.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"],
+                        inp["seq_lens"], out, num_kv_heads=w.num_kv_heads, page_size=w.page_size,
+                        kv_layout=w.kv_layout)
