@@ -36,6 +36,12 @@ times the latent-attention projections around the decode (pkv_head_matmul:
 BMM1 with W_UK_T, the up-projection with W_UV) for the latent workload's 32
 decode tokens and 64 heads; value = bytes read + written / wall time (the
 weights dominate).
+
+    python bench.py --workload merge_chunked_prefill
+
+times the merge of two attention results by their log-sum-exps
+(pkv_merge_attn_states) for a chunked prefill of 8192 tokens, 128 heads,
+head dim 128; value = bytes read + written / wall time.
 """
 from __future__ import annotations
 
@@ -114,6 +120,8 @@ def main():
         return bench_insert(args)
     if args.workload in PROJ_WORKLOADS:
         return bench_proj(args)
+    if args.workload in MERGE_WORKLOADS:
+        return bench_merge(args)
 
     import paged_kv_attention_pages_amd as pkv
     from paged_kv_attention_pages_amd import synth
@@ -297,6 +305,68 @@ def bench_proj(args):
         "config": {"workload": args.workload, "tokens": M, "heads": H, "k": K, "n": N,
                    "bytes_per_call": nbytes, "flops_per_call": flops, "weight_replicas": n_rep},
         "roofline": {"kernel": "head matmul", "bound": "hbm",
+                     "achieved": round(nbytes / (kern_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": nbytes,
+                     "launch_us_mean": round(kern_ms * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+MERGE_WORKLOADS = {
+    # chunked prefill of 8192 new tokens, 128 heads, value head dim 128
+    "merge_chunked_prefill": dict(N=8192, H=128, D=128),
+}
+
+
+def bench_merge(args):
+    import paged_kv_attention_pages_amd as pkv
+    cfg = MERGE_WORKLOADS[args.workload]
+    N, H, D = cfg["N"], cfg["H"], cfg["D"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev).manual_seed(1)
+    po = torch.randn(N, H, D, generator=g, device=dev).to(torch.bfloat16)
+    so = torch.randn(N, H, D, generator=g, device=dev).to(torch.bfloat16)
+    pl = torch.randn(H, N, generator=g, device=dev) * 4
+    sl = torch.randn(H, N, generator=g, device=dev) * 4
+    out = torch.empty_like(so)
+    lse = torch.empty_like(sl)
+    # two outputs read, one written; two log-sum-exps read, one written
+    nbytes = 3 * N * H * D * 2 + 3 * N * H * 4
+
+    def call():
+        pkv.merge_attn_states(out, po, pl, so, sl, N, lse)
+
+    K_, W_ = args.steps, args.warmup
+    for _ in range(W_):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K_):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K_
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K_)]
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    kern_ms = statistics.fmean(a.elapsed_time(b) for a, b in ev)
+    value = nbytes / (ms * 1e-3) / 1e9
+    print(f"[bench] {args.workload}: {ms * 1e3:.2f} us/call wall, evented {kern_ms * 1e3:.2f} us, "
+          f"{value:.0f} GB/s", file=sys.stderr, flush=True)
+    rec = {
+        "metric": "attention-state merge GB/s (bytes read + written) + us/call",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K_, "warmup": W_,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "us_per_call": round(ms * 1e3, 2),
+        "config": {"workload": args.workload, "tokens": N, "heads": H, "head_dim": D,
+                   "bytes_per_call": nbytes},
+        "roofline": {"kernel": "merge states", "bound": "hbm",
                      "achieved": round(nbytes / (kern_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": None, "algorithmic_bytes": nbytes,

@@ -291,6 +291,28 @@ pkv_status pkv_head_matmul(const void* x, int64_t x_stride_m, int64_t x_stride_h
                            void* y, int64_t y_stride_m, int64_t y_stride_h, int M, int H, int K,
                            int N, int dtype, void* stream);
 
+/* ---- merging attention results over disjoint key sets --------------- */
+
+/* vLLM Kimi-K3 MLA page, chunked prefill `merge_attn_states(output,
+ * prefix_output, prefix_lse, suffix_output, suffix_lse,
+ * prefill_tokens_with_context)`: for token n < N and head h < H, with the
+ * natural-log log-sum-exps lp = prefix_lse(n, h), ls = suffix_lse(n, h),
+ * M = max(lp, ls) and w = e^(lse - M):
+ *   out[n, h] = (prefix_out[n, h] w_p + suffix_out[n, h] w_s) / (w_p + w_s)
+ * and, when out_lse != NULL, out_lse(n, h) = M + log(w_p + w_s).  Tokens
+ * n >= num_tokens_with_prefix take the suffix alone (prefix arrays then need
+ * only num_tokens_with_prefix rows).  An -inf log-sum-exp contributes
+ * nothing; both -inf give zeros (and -inf).  out, prefix_out, suffix_out:
+ * [N, H, D] contiguous, dtype PKV_BF16 or PKV_F16, D a multiple of 8,
+ * 16-byte aligned; log-sum-exps fp32 with element (n, h) at
+ * lse + n * lse_stride_n + h * lse_stride_h (e.g. [H, N]: strides 1, N).
+ * One launch on `stream`. */
+pkv_status pkv_merge_attn_states(void* out, const void* prefix_out, const float* prefix_lse,
+                                 const void* suffix_out, const float* suffix_lse, float* out_lse,
+                                 int64_t lse_stride_n, int64_t lse_stride_h, int num_tokens,
+                                 int num_heads, int head_dim, int num_tokens_with_prefix,
+                                 int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,6 +14,7 @@ brute-force attention on gathered pages, closed forms and invariants.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 import threading
@@ -239,3 +240,41 @@ def mla_materialised(q_nope, q_pe, kv_cache, page_table, seq_lens, w_uk_t, w_uv,
             logits = softmax_scale * (k_nope @ qn[b, h] + k_pe @ qp[b, h])
             out[b, h] = torch.softmax(logits, dim=0) @ v
     return out
+
+
+def merge_attn_states(prefix_out, prefix_lse, suffix_out, suffix_lse, num_tokens_with_prefix=None):
+    """fp64 merge of two attention results by their natural-log log-sum-exps.
+
+    vLLM Kimi-K3 MLA page, chunked prefill `merge_attn_states`: with
+    M = max(lp, ls) and w = e^(lse - M), out = (o_p w_p + o_s w_s) / (w_p + w_s)
+    and lse = M + log(w_p + w_s); tokens at or past num_tokens_with_prefix
+    take the suffix alone; both -inf give zeros and -inf.  Outputs [N, H, D],
+    log-sum-exps [H, N].  Returns (out fp64 [N, H, D], lse fp64 [H, N]).
+    """
+    so = suffix_out.detach().to("cpu", torch.float64)
+    sl = suffix_lse.detach().to("cpu", torch.float64)
+    N, H, D = so.shape
+    n_pre = N if num_tokens_with_prefix is None else int(num_tokens_with_prefix)
+    po = torch.zeros_like(so)
+    pl = torch.full_like(sl, float("-inf"))
+    if n_pre > 0:
+        po[:n_pre] = prefix_out.detach().to("cpu", torch.float64)[:n_pre]
+        pl[:, :n_pre] = prefix_lse.detach().to("cpu", torch.float64)[:, :n_pre]
+    out = torch.zeros_like(so)
+    lse = torch.full_like(sl, float("-inf"))
+    for n in range(N):
+        for h in range(H):
+            lp, ls = float(pl[h, n]), float(sl[h, n])
+            M = max(lp, ls)
+            if M == float("-inf"):
+                continue
+            wp = 0.0 if lp == float("-inf") else math.exp(lp - M)
+            ws = 0.0 if ls == float("-inf") else math.exp(ls - M)
+            acc = torch.zeros(D, dtype=torch.float64)
+            if wp:
+                acc += po[n, h] * wp
+            if ws:
+                acc += so[n, h] * ws
+            out[n, h] = acc / (wp + ws)
+            lse[h, n] = M + math.log(wp + ws)
+    return out, lse

@@ -116,6 +116,10 @@ def lib():
                                               ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int, _vp]
+                L.pkv_merge_attn_states.restype = ctypes.c_int
+                L.pkv_merge_attn_states.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
+                                                    ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]
                 L.pkv_cache_insert.restype = ctypes.c_int
                 L.pkv_cache_insert.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                                _vp, _vp, _vp, _vp, ctypes.POINTER(InsertDims)]
@@ -441,3 +445,40 @@ def head_matmul(x, w, y=None, *, stream=None):
                                    y.stride(1), M, H, K, N, _DTYPE[x.dtype], ctypes.c_void_p(stream))
     _check(st)
     return y
+
+
+def merge_attn_states(output, prefix_output, prefix_lse, suffix_output, suffix_lse,
+                      num_tokens_with_prefix=None, output_lse=None, *, stream=None):
+    """Merge two attention results over disjoint key sets by their natural-log
+    log-sum-exps, in place into ``output`` (one launch).
+
+    outputs [N, H, D] contiguous (bf16 or f16); log-sum-exps float32 [H, N]
+    (any strides).  Tokens at or past ``num_tokens_with_prefix`` (default N)
+    take the suffix alone.  Returns ``output``.
+    """
+    if output.device.type != "cuda":
+        raise PkvError(1, "merge_attn_states runs on the GPU only")
+    N, H, D = output.shape
+    n_pre = N if num_tokens_with_prefix is None else int(num_tokens_with_prefix)
+    for name, t, rows in (("prefix_output", prefix_output, n_pre), ("suffix_output", suffix_output, N)):
+        if t is None and rows == 0:
+            continue
+        if t is None or t.dtype != output.dtype or tuple(t.shape[1:]) != (H, D) or t.shape[0] < rows \
+                or not t.is_contiguous():
+            raise PkvError(1, f"{name} must be contiguous [>= {rows}, {H}, {D}] of output's dtype")
+    for name, t in (("prefix_lse", prefix_lse), ("suffix_lse", suffix_lse), ("output_lse", output_lse)):
+        if t is not None and (t.dtype != torch.float32 or t.dim() != 2 or t.shape[0] != H):
+            raise PkvError(1, f"{name} must be float32 [{H}, tokens]")
+    if output_lse is not None and output_lse.stride() != suffix_lse.stride():
+        raise PkvError(1, "output_lse must have suffix_lse's strides")
+    if prefix_lse is not None and prefix_lse.stride() != suffix_lse.stride():
+        raise PkvError(1, "prefix_lse and suffix_lse must share strides")
+    if stream is None:
+        stream = torch.cuda.current_stream(output.device).cuda_stream
+    with torch.cuda.device(output.device):
+        st = lib().pkv_merge_attn_states(
+            _ptr(output), _ptr(prefix_output), _ptr(prefix_lse), _ptr(suffix_output), _ptr(suffix_lse),
+            _ptr(output_lse), suffix_lse.stride(1), suffix_lse.stride(0), N, H, D, n_pre,
+            _DTYPE[output.dtype], ctypes.c_void_p(stream))
+    _check(st)
+    return output

@@ -564,4 +564,46 @@ pkv_status pkv_head_matmul(const void* x, int64_t xs_m, int64_t xs_h, const void
   return PKV_OK;
 }
 
+pkv_status pkv_merge_attn_states(void* out, const void* o_p, const float* lse_p, const void* o_s,
+                                 const float* lse_s, float* lse_out, int64_t lse_sn, int64_t lse_sh,
+                                 int N, int H, int D, int n_prefix, int dtype, void* stream) {
+  if (N < 0 || H < 1 || D < 8 || D % 8 || n_prefix < 0 || n_prefix > N)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "merge_attn_states needs N >= 0, H >= 1, head_dim a "
+                                          "multiple of 8 and 0 <= num_tokens_with_prefix <= N "
+                                          "(got N %d, H %d, D %d, prefix %d)", N, H, D, n_prefix);
+  if (dtype != PKV_F16 && dtype != PKV_BF16)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "merge_attn_states dtype must be float16 or bfloat16");
+  if (lse_sn < 0 || lse_sh < 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "log-sum-exp strides must be non-negative");
+  if (N == 0) {
+    g_err.clear();
+    return PKV_OK;
+  }
+  if (!out || !o_s || !lse_s || (n_prefix > 0 && (!o_p || !lse_p)))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "out, suffix_out, suffix_lse (and the prefix arrays when "
+                                          "num_tokens_with_prefix > 0) must not be NULL");
+  if (misaligned(out, 16) || misaligned(o_p, 16) || misaligned(o_s, 16) || misaligned(lse_p, 4) ||
+      misaligned(lse_s, 4) || misaligned(lse_out, 4))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "outputs must be 16-byte and log-sum-exps 4-byte aligned");
+  if ((int64_t)N * H * (D / 8) >= ((int64_t)1 << 31))
+    return fail(PKV_ERR_UNSUPPORTED, "merge_attn_states: too many elements (limit 2^34)");
+  pkv::MergeParams p{};
+  p.out = out;
+  p.o_p = o_p;
+  p.o_s = o_s;
+  p.lse_p = lse_p;
+  p.lse_s = lse_s;
+  p.lse_out = lse_out;
+  p.lse_sn = lse_sn;
+  p.lse_sh = lse_sh;
+  p.N = N;
+  p.H = H;
+  p.D = D;
+  p.n_prefix = n_prefix;
+  const hipError_t e = pkv::launch_merge_states(dtype, p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge_attn_states launch failed: %s", hipGetErrorString(e));
+  g_err.clear();
+  return PKV_OK;
+}
+
 }  // extern "C"

@@ -45,6 +45,19 @@ struct HeadMatmulParams {
 };
 hipError_t launch_head_matmul(int dtype, const HeadMatmulParams& p, hipStream_t s);
 
+// Merge of two attention results by their log-sum-exps (natural log).
+struct MergeParams {
+  void* out;                  // [N, H, D]
+  const void* o_p;            // [n_prefix, H, D] prefix results
+  const void* o_s;            // [N, H, D] suffix results
+  const float* lse_p;         // element (n, h) at n * lse_sn + h * lse_sh
+  const float* lse_s;
+  float* lse_out;             // same layout, or null
+  int64_t lse_sn, lse_sh;
+  int N, H, D, n_prefix;
+};
+hipError_t launch_merge_states(int dtype, const MergeParams& p, hipStream_t s);
+
 // Log-sum-exp merge of the split partials of every sequence that needed
 // more than one split (zeros for sequences with nothing visible).
 hipError_t launch_combine(int q_dtype, const Params& p, hipStream_t s);

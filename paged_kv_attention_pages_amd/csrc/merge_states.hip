@@ -1,0 +1,71 @@
+// merge_states.hip -- merge of two attention results over disjoint key sets
+// by their log-sum-exps.
+//
+// vLLM `models/kimi_k3/nvidia/mla` page, chunked prefill: the attention of
+// the new tokens over the cached context (prefix) and over themselves
+// (suffix) are merged with `merge_attn_states(output, prefix_output,
+// prefix_lse, suffix_output, suffix_lse, prefill_tokens_with_context)`.
+// With M = max(lse_p, lse_s) and weights w = e^(lse - M):
+//   out = (o_p w_p + o_s w_s) / (w_p + w_s),   lse_out = M + log(w_p + w_s)
+// Tokens at or past the number with a prefix take the suffix alone.  Both
+// log-sum-exps -inf (nothing visible) give zeros.
+//
+// Work item: 8 elements (16 bytes) of one (token, head) row; 256 per block.
+#include "pkv_device.h"
+#include "kernels.h"
+
+namespace pkv {
+
+namespace {
+
+template <int QT>
+__global__ __launch_bounds__(256) void merge_states_kernel(MergeParams p) {
+  const uint32_t per_row = (uint32_t)p.D >> 3;
+  const uint32_t item = blockIdx.x * 256u + threadIdx.x;
+  if (item >= (uint32_t)p.N * (uint32_t)p.H * per_row) return;
+  const uint32_t row = item / per_row, d = (item - row * per_row) * 8;
+  const uint32_t n = row / (uint32_t)p.H, h = row - n * (uint32_t)p.H;
+  const bool has_p = (int)n < p.n_prefix;
+  const float lp = has_p ? p.lse_p[(int64_t)n * p.lse_sn + (int64_t)h * p.lse_sh] : -__builtin_inff();
+  const float ls = p.lse_s[(int64_t)n * p.lse_sn + (int64_t)h * p.lse_sh];
+  const float M = fmaxf(lp, ls);
+  float wp = 0.f, ws = 0.f;
+  if (M != -__builtin_inff()) {
+    wp = lp == -__builtin_inff() ? 0.f : __expf(lp - M);
+    ws = ls == -__builtin_inff() ? 0.f : __expf(ls - M);
+  }
+  const float den = wp + ws;
+  const float a = den > 0.f ? wp / den : 0.f, b = den > 0.f ? ws / den : 0.f;
+  const int64_t off = (int64_t)row * p.D + d;
+  const uint4 vs = *(const uint4*)((const uint16_t*)p.o_s + off);
+  const uint4 vp = has_p ? *(const uint4*)((const uint16_t*)p.o_p + off) : make_uint4(0, 0, 0, 0);
+  const uint32_t sw[4] = {vs.x, vs.y, vs.z, vs.w}, pw[4] = {vp.x, vp.y, vp.z, vp.w};
+  uint32_t ow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float2 s2 = unpack2<QT>(sw[i]), p2 = unpack2<QT>(pw[i]);
+    // a zero weight drops its side entirely (the other side may hold anything)
+    const float x = (a != 0.f ? p2.x * a : 0.f) + (b != 0.f ? s2.x * b : 0.f);
+    const float y = (a != 0.f ? p2.y * a : 0.f) + (b != 0.f ? s2.y * b : 0.f);
+    ow[i] = pack2<QT>(x, y);
+  }
+  *(uint4*)((uint16_t*)p.out + off) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  if (p.lse_out != nullptr && d == 0)
+    p.lse_out[(int64_t)n * p.lse_sn + (int64_t)h * p.lse_sh] = den > 0.f ? M + __logf(den) : -__builtin_inff();
+}
+
+}  // namespace
+
+hipError_t launch_merge_states(int dtype, const MergeParams& p, hipStream_t s) {
+  const int64_t items = (int64_t)p.N * p.H * (p.D / 8);
+  if (items == 0) return hipSuccess;
+  if (items >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((items + 255) / 256));
+  if (dtype == kBF16)
+    hipLaunchKernelGGL((merge_states_kernel<kBF16>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((merge_states_kernel<kF16>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

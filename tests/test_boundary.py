@@ -262,3 +262,48 @@ def test_cache_insert_null_tensors_and_bad_scale():
     # nothing to insert: no device call, success
     assert L.pkv_cache_insert(None, None, None, None, None, None, 1.0, None, None, None, None, None,
                               ctypes.byref(_insert_dims(num_tokens=0))) == 0
+
+
+@pytest.mark.parametrize("M, H, K, N, dtype, msg", [
+    (-1, 4, 32, 64, 1, "M >= 0"),
+    (4, 0, 32, 64, 1, "H >= 1"),
+    (4, 4, 48, 64, 1, "multiple of 32"),
+    (4, 4, 32, 96, 1, "multiple of 64"),
+    (4, 4, 32, 64, 2, "float16 or bfloat16"),
+])
+def test_head_matmul_rejects_bad_sizes(M, H, K, N, dtype, msg):
+    L = pkv.lib()
+    st = L.pkv_head_matmul(None, 8 * 32, 32, None, None, 64, 64, M, H, K, N, dtype, None)
+    assert st == 1 and msg in L.pkv_last_error().decode()
+
+
+def test_head_matmul_rejects_strides_and_nulls():
+    L = pkv.lib()
+    assert L.pkv_head_matmul(None, 12, 32, None, None, 64, 64, 4, 4, 32, 64, 1, None) == 1
+    assert "strides" in L.pkv_last_error().decode()
+    assert L.pkv_head_matmul(None, 128, 32, None, None, 64, 64, 4, 4, 32, 64, 1, None) == 1
+    assert "must not be NULL" in L.pkv_last_error().decode()
+    assert L.pkv_head_matmul(None, 128, 32, None, None, 64, 64, 0, 4, 32, 64, 1, None) == 0
+
+
+@pytest.mark.parametrize("N, H, D, n_pre, dtype, msg", [
+    (-1, 2, 64, 0, 1, "N >= 0"),
+    (4, 0, 64, 0, 1, "H >= 1"),
+    (4, 2, 60, 0, 1, "multiple of 8"),
+    (4, 2, 64, 5, 1, "num_tokens_with_prefix <= N"),
+    (4, 2, 64, -1, 1, "num_tokens_with_prefix <= N"),
+    (4, 2, 64, 2, 2, "float16 or bfloat16"),
+])
+def test_merge_attn_states_rejects_bad_sizes(N, H, D, n_pre, dtype, msg):
+    L = pkv.lib()
+    st = L.pkv_merge_attn_states(None, None, None, None, None, None, 1, N, N, H, D, n_pre, dtype, None)
+    assert st == 1 and msg in L.pkv_last_error().decode()
+
+
+def test_merge_attn_states_nulls_and_empty():
+    L = pkv.lib()
+    assert L.pkv_merge_attn_states(None, None, None, None, None, None, 1, 4, 4, 2, 64, 2, 1, None) == 1
+    assert "must not be NULL" in L.pkv_last_error().decode()
+    assert L.pkv_merge_attn_states(None, None, None, None, None, None, -1, 4, 4, 2, 64, 2, 1, None) == 1
+    assert "non-negative" in L.pkv_last_error().decode()
+    assert L.pkv_merge_attn_states(None, None, None, None, None, None, 1, 0, 0, 2, 64, 0, 1, None) == 0

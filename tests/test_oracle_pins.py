@@ -617,3 +617,52 @@ def test_head_matmul_brute_force():
             for n in range(5):
                 want = math.fsum(xs[m][h][k] * ws[h][k][n] for k in range(8))
                 assert abs(y[m, h, n].item() - want) <= 1e-12
+
+
+# ---------------------------------------------------------------- log-sum-exp merge
+
+def _dense_attn_with_lse(q, K, V, scale):
+    logits = scale * (K @ q)
+    lse = torch.logsumexp(logits, dim=0)
+    return torch.softmax(logits, dim=0) @ V, lse
+
+
+def test_merge_of_two_key_sets_equals_attention_over_their_union():
+    # attention over keys [0, a) and [a, L) separately, merged by their
+    # log-sum-exps, equals attention over [0, L) (dense, torch softmax)
+    g = torch.Generator().manual_seed(41)
+    N, H, D, L, a = 3, 2, 16, 40, 13
+    Q = torch.randn(N, H, D, generator=g, dtype=torch.float64)
+    K = torch.randn(H, L, D, generator=g, dtype=torch.float64)
+    V = torch.randn(H, L, D, generator=g, dtype=torch.float64)
+    po, so, full = (torch.zeros(N, H, D, dtype=torch.float64) for _ in range(3))
+    pl, sl = torch.zeros(H, N, dtype=torch.float64), torch.zeros(H, N, dtype=torch.float64)
+    for n in range(N):
+        for h in range(H):
+            po[n, h], pl[h, n] = _dense_attn_with_lse(Q[n, h], K[h, :a], V[h, :a], 0.3)
+            so[n, h], sl[h, n] = _dense_attn_with_lse(Q[n, h], K[h, a:], V[h, a:], 0.3)
+            full[n, h], _ = _dense_attn_with_lse(Q[n, h], K[h], V[h], 0.3)
+    out, lse = oracle.merge_attn_states(po, pl, so, sl)
+    assert torch.allclose(out, full, rtol=0, atol=1e-12)
+    for n in range(N):
+        for h in range(H):
+            want = torch.logsumexp(0.3 * (K[h] @ Q[n, h]), dim=0)
+            assert abs(float(lse[h, n]) - float(want)) < 1e-12
+
+
+def test_merge_special_cases():
+    g = torch.Generator().manual_seed(42)
+    po = torch.randn(4, 2, 8, generator=g, dtype=torch.float64)
+    so = torch.randn(4, 2, 8, generator=g, dtype=torch.float64)
+    sl = torch.randn(2, 4, generator=g, dtype=torch.float64)
+    pl = sl.clone()
+    pl[0, 1] = float("-inf")                          # empty prefix: the suffix alone
+    out, lse = oracle.merge_attn_states(po, pl, so, sl, num_tokens_with_prefix=3)
+    assert torch.equal(out[1, 0], so[1, 0]) and lse[0, 1] == sl[0, 1]
+    assert torch.equal(out[3], so[3])                 # past the prefixed tokens
+    assert torch.allclose(out[0], (po[0] + so[0]) / 2, rtol=0, atol=1e-15)   # equal weights
+    sym, _ = oracle.merge_attn_states(so, sl, po, pl.clone().masked_fill(torch.isinf(pl), 0), 3)
+    assert torch.allclose(sym[0], out[0], rtol=0, atol=1e-15)
+    both, lse2 = oracle.merge_attn_states(po, torch.full_like(sl, float("-inf")), so,
+                                          torch.full_like(sl, float("-inf")))
+    assert torch.equal(both, torch.zeros_like(both)) and torch.isinf(lse2).all()
