@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 4
+#define PKV_ABI_VERSION 5
 
 typedef enum {
   PKV_OK = 0,
@@ -162,6 +162,9 @@ typedef struct pkv_plan_info {
   uint64_t workspace_bytes;    /* bytes the call needs                      */
   int32_t single_launch;       /* 1: the split kernel merges its partials
                                   itself (no combine kernel); ABI 3         */
+  int32_t waves_per_workgroup; /* matrix-core stream-K: waves per workgroup,
+                                  each streaming the same tokens of another
+                                  KV head; ABI 5                            */
 } pkv_plan_info;
 
 /* ABI version (PKV_ABI_VERSION of the built library). */

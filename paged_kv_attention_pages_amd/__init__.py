@@ -70,7 +70,8 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("split_pages", ctypes.c_int32),
                 ("max_splits", ctypes.c_int32), ("rows", ctypes.c_int32),
                 ("ctas_per_split_grid", ctypes.c_int32), ("num_cus", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_uint64), ("single_launch", ctypes.c_int32)]
+                ("workspace_bytes", ctypes.c_uint64), ("single_launch", ctypes.c_int32),
+                ("waves_per_workgroup", ctypes.c_int32)]
 
 
 _lib = None

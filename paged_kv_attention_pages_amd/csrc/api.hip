@@ -60,6 +60,7 @@ struct Plan {
   int max_splits;
   int num_cus;
   int sk_waves;        // > 0: stream-K over this many persistent waves
+  int sk_hb;           // matrix-core stream-K: waves per workgroup, one KV head each
   size_t ws_o_bytes;   // partial outputs
   size_t ws_ml_off;    // offset of (max, sum) pairs
   size_t ws_cnt_off;   // offset of the per-unit counters (single-launch merge)
@@ -178,6 +179,7 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
   pl->max_splits = (int)S;
   pl->num_cus = cus;
   pl->sk_waves = 0;
+  pl->sk_hb = 1;
   pl->fused = false;
   pl->ws_cnt_off = 0;
   // Stream-K schedule (matrix-core path, batch <= 256, no forced split size):
@@ -195,6 +197,18 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
     const int64_t per_cu = path == PKV_PATH_MFMA_MLA ? 1 : d->kv_dtype == PKV_FP8_E4M3 ? 8 : 4;
     const int64_t W = (opts && opts->target_ctas > 0) ? opts->target_ctas : per_cu * cus;
     pl->sk_waves = (int)std::min<int64_t>(W, 1 << 20);
+    // The waves of one workgroup stream the same tokens of sk_hb KV heads
+    // side by side (the unit order is KV-head-major and Hkv divides the wave
+    // count), so in an NHD cache the heads' pieces of each token row are read
+    // together: up to one CU's resident waves (at most 8), a divisor of Hkv.
+    pl->sk_hb = 1;
+    const int64_t resident = pl->sk_waves >= cus ? std::min<int64_t>(8, pl->sk_waves / cus) : 8;
+    if (path == PKV_PATH_MFMA && pl->sk_waves % Hkv == 0)
+      for (int h = (int)std::min<int64_t>(resident, Hkv); h > 1; --h)
+        if (Hkv % h == 0) {
+          pl->sk_hb = h;
+          break;
+        }
     pl->split_pages = 0;
     pl->max_splits = 0;
     const size_t nrow = (size_t)2 * pl->sk_waves * R;
@@ -304,6 +318,7 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
   p.split_pages = pl.split_pages;
   p.max_splits = pl.max_splits;
   p.sk_waves = pl.sk_waves;
+  p.sk_hb = pl.sk_hb;
   p.sk_shift = pl.path == PKV_PATH_MFMA_MLA ? 5 : 4;
   p.qk_scale_log2 = (float)((double)q_scale * (double)kv_scale / std::sqrt((double)Dk) *
                             1.4426950408889634);
@@ -367,6 +382,7 @@ pkv_status pkv_query_plan(const pkv_dims* dims, int num_kv_heads, int page_size,
   info->num_cus = pl.num_cus;
   info->workspace_bytes = pl.ws_bytes;
   info->single_launch = pl.fused ? 1 : 0;
+  info->waves_per_workgroup = pl.path == PKV_PATH_MFMA_MLA ? 8 : pl.sk_waves > 0 ? pl.sk_hb : 1;
   g_err.clear();
   return PKV_OK;
 }

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void combine_sk_kernel(Params p) {
     for (int d = lane; d < p.Dv; d += 64) store_out1<QT>(p, ob + d, 0.f);
     return;
   }
-  const int64_t us = (int64_t)pre * p.Hkv + (int64_t)kvh * n, ue = us + n;
+  const int64_t us = sk_unit_start(S, kvh, pre), ue = us + n;
   const int w0 = sk_wave_of(S.T, us, W), w1 = sk_wave_of(S.T, ue - 1, W);
   if (w0 == w1) return;
   const int64_t slot0 = sk_wave_start(S.T, w0, W) == us ? 2 * (int64_t)w0 : 2 * (int64_t)w0 + 1;

@@ -33,6 +33,7 @@ struct Params {
   int sk_waves;               // > 0: stream-K schedule over that many waves
                               // (or workgroups, for the latent-cache kernel)
   int sk_shift;               // stream-K tiles are 1 << sk_shift tokens
+  int sk_hb;                  // matrix-core stream-K: waves (KV heads) per workgroup
   float qk_scale_log2;        // q_scale * kv_scale / sqrt(Dqk) * log2(e)
   float out_scale;            // kv_scale (V dequantisation, applied once)
   // device-resident scales (null: the host values above hold)
@@ -118,16 +119,24 @@ __device__ __forceinline__ int wave_scan(int x) {
 }
 
 // Stream-K tile space: unit (b, kvh) owns the visible tiles of sequence b
-// for KV head kvh; units are laid end to end in (b, kvh) order, so unit
-// (b, kvh) starts at Hkv * pre_b + kvh * n_b with pre_b the tiles of the
-// sequences before b.  Wave w of W takes tiles [w T / W, (w+1) T / W).
+// for KV head kvh; units are laid end to end KV-head-major, so unit (b, kvh)
+// starts at kvh * T1 + pre_b, with T1 the tiles of one KV head over all
+// sequences and pre_b the tiles of the sequences before b.  Wave w of W takes
+// tiles [w T / W, (w+1) T / W), T = Hkv T1; when Hkv divides W, waves w and
+// w + k W / Hkv take the same tiles of KV heads kvh and kvh + k.
 // Lane l holds pre_b and n_b of sequences b = l + 64 c (c < 4: B <= 256).
 constexpr int kSkMaxBatch = 256;
 struct SkSched {
   int64_t T;     // total tiles
+  int T1;        // tiles of one KV head
   int pre[4];    // exclusive prefix of tiles per sequence (lane's sequences)
   int cnt[4];    // tiles per sequence
 };
+
+// First global tile of unit (b, kvh), given pre_b.
+__device__ __forceinline__ int64_t sk_unit_start(const SkSched& s, int kvh, int pre) {
+  return (int64_t)kvh * s.T1 + pre;
+}
 
 __device__ __forceinline__ SkSched sk_schedule(const Params& p) {
   SkSched s;
@@ -143,6 +152,7 @@ __device__ __forceinline__ SkSched sk_schedule(const Params& p) {
     s.cnt[c] = n;
     carry = __builtin_amdgcn_readlane(inc, 63);
   }
+  s.T1 = carry;
   s.T = (int64_t)carry * p.Hkv;
   return s;
 }
@@ -185,23 +195,23 @@ __device__ __forceinline__ void sk_seq_of(const SkSched& s, int b, int* pre, int
 }
 
 __device__ __forceinline__ SkUnit sk_locate(const Params& p, const SkSched& s, int64_t x) {
-  // last sequence whose first tile is <= x (it has tiles, since x < T)
+  SkUnit u;
+  u.kvh = (int)(x / s.T1);
+  const int xr = (int)(x - (int64_t)u.kvh * s.T1);
+  // last sequence whose first tile is <= xr (it has tiles, since xr < T1)
   int best = 0;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int b = (threadIdx.x & 63) + 64 * c;
-    const bool ok = b < p.B && (int64_t)s.pre[c] * p.Hkv <= x;
+    const bool ok = b < p.B && s.pre[c] <= xr;
     const uint64_t m = __ballot(ok);
     if (m != 0) best = 64 * c + 63 - __builtin_clzll(m);
   }
-  SkUnit u;
   u.b = best;
   int pre, n;
   sk_seq_of(s, best, &pre, &n);
-  const int64_t off = x - (int64_t)pre * p.Hkv;
-  u.kvh = (int)(off / n);
   u.ntiles = n;
-  u.start = (int64_t)pre * p.Hkv + (int64_t)u.kvh * n;
+  u.start = sk_unit_start(s, u.kvh, pre);
   return u;
 }
 

@@ -497,10 +497,18 @@ __global__ __launch_bounds__(64) void split_mfma16_kernel(Params p) {
 template <int QT, int KT, int D, bool FUSED>
 // (two waves per SIMD: the register budget keeps the accumulators in
 // architected VGPRs instead of moving them through AGPRs every tile)
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma16_sk_kernel(Params p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma16_sk_kernel(Params p) {
   resolve_scales(p);
   const SkSched S = sk_schedule(p);
-  const int w = blockIdx.x, W = sk_waves_eff(S.T, gridDim.x);
+  const int W = sk_waves_eff(S.T, p.sk_waves);
+  // workgroup (head group hg, position j) of sk_hb waves: wave i takes share
+  // j of KV head hg * sk_hb + i's part of the tile stream (W / Hkv waves per
+  // head), i.e. the same tokens as its neighbours, of another KV head
+  int w = blockIdx.x;
+  if (p.sk_hb > 1) {
+    const int W1 = p.sk_waves / p.Hkv, hg = blockIdx.x / W1, j = blockIdx.x - hg * W1;
+    w = (hg * p.sk_hb + (int)(threadIdx.x >> 6)) * W1 + j;
+  }
   if (w >= W) return;
   const int64_t x0 = sk_wave_start(S.T, w, W), x1 = sk_wave_start(S.T, w + 1, W);
   if (FUSED) zero_empty_units(p, S, w, W);
@@ -548,10 +556,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void sp
 
 template <int QT, int KT, int D>
 hipError_t launch_split_mfma16(const Params& p, hipStream_t stream) {
-  if (p.sk_waves > 0 && p.fused) {
-    hipLaunchKernelGGL((split_mfma16_sk_kernel<QT, KT, D, true>), dim3(p.sk_waves), dim3(64), 0, stream, p);
-  } else if (p.sk_waves > 0) {
-    hipLaunchKernelGGL((split_mfma16_sk_kernel<QT, KT, D, false>), dim3(p.sk_waves), dim3(64), 0, stream, p);
+  if (p.sk_waves > 0) {
+    const dim3 grid(p.sk_waves / p.sk_hb), block(64 * p.sk_hb);
+    if (p.fused)
+      hipLaunchKernelGGL((split_mfma16_sk_kernel<QT, KT, D, true>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((split_mfma16_sk_kernel<QT, KT, D, false>), grid, block, 0, stream, p);
   } else {
     dim3 grid(p.max_splits, p.Hkv, p.B);
     hipLaunchKernelGGL((split_mfma16_kernel<QT, KT, D>), grid, dim3(64), 0, stream, p);
@@ -562,6 +572,9 @@ hipError_t launch_split_mfma16(const Params& p, hipStream_t stream) {
 hipError_t launch_split_mfma16(int q_dtype, int kv_dtype, int D, const Params& p, hipStream_t s) {
   if (p.sk_waves == 0 && p.split_pages > 64) return hipErrorInvalidValue;
   if (p.sk_waves > 0 && p.B > kSkMaxBatch) return hipErrorInvalidValue;
+  if (p.sk_waves > 0 && (p.sk_hb < 1 || p.sk_hb > 8 || p.sk_waves % p.sk_hb ||
+                         (p.sk_hb > 1 && (p.sk_waves % p.Hkv || p.Hkv % p.sk_hb))))
+    return hipErrorInvalidValue;
 #define PKV_CASE(QT, KT, DD) \
   if (q_dtype == QT && kv_dtype == KT && D == DD) return launch_split_mfma16<QT, KT, DD>(p, s);
   PKV_CASE(kBF16, kBF16, 128)

@@ -490,9 +490,11 @@ __global__ __launch_bounds__(kThreads) void split_mla_sk_kernel(Params p) {
   __shared__ int sk_pre[kSkMaxBatch], sk_cnt[kSkMaxBatch];
   const int lane = threadIdx.x & 63;
   int64_t T;
+  int T1;
   {
     const SkSched S = sk_schedule(p);
     T = S.T;
+    T1 = S.T1;
     if (wave_id() == 0) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -506,24 +508,24 @@ __global__ __launch_bounds__(kThreads) void split_mla_sk_kernel(Params p) {
   if (wg >= W) return;
   // the host keeps the tile stream under 2^31 tiles for this kernel
   const int x0 = (int)sk_wave_start(T, wg, W), x1 = (int)sk_wave_start(T, wg + 1, W);
-  const int Hkv = p.Hkv;
   const LdsOff L = lds_offsets();
   for (int x = x0; x < x1;) {
     Piece P;
     QRegs Q;
     Acc A;
-    // unit holding global tile x: the last sequence whose first tile is <= x
+    // unit holding global tile x (units KV-head-major): its KV head, then
+    // the last sequence whose first tile is <= x within that head's tiles
+    const int kvh = x / T1, xr = x - kvh * T1;
     int b = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int bb = lane + 64 * c;
-      const bool ok = bb < p.B && sk_pre[bb] * Hkv <= x;
+      const bool ok = bb < p.B && sk_pre[bb] <= xr;
       const uint64_t m = __ballot(ok);
       if (m != 0) b = 64 * c + 63 - __builtin_clzll(m);
     }
     const int pre = sk_pre[b], ntiles = sk_cnt[b];
-    const int kvh = (x - pre * Hkv) / ntiles;
-    const int ustart = pre * Hkv + kvh * ntiles;
+    const int ustart = kvh * T1 + pre;
     const int seg_end = min(x1, ustart + ntiles);
     const SeqGeom sg = seq_geom(p, b);
     const int tile0 = sg.lo >> kTileShift;

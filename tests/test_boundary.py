@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (pkv_\w+)", out))
     assert set(names) <= exported, set(names) - exported
-    assert pkv.lib().pkv_abi_version() == 4
+    assert pkv.lib().pkv_abi_version() == 5
 
 
 def test_struct_layouts_match_header(tmp_path):
@@ -57,6 +57,7 @@ int main(void) {
   printf("pkv_insert_dims %zu\\n", sizeof(pkv_insert_dims));
   F(pkv_insert_dims, num_q_heads) F(pkv_insert_dims, cache_dtype)
   F(pkv_plan_info, workspace_bytes) F(pkv_plan_info, num_cus) F(pkv_plan_info, single_launch)
+  F(pkv_plan_info, waves_per_workgroup)
   return 0;
 }
 """)
@@ -82,6 +83,7 @@ int main(void) {
     assert int(got["pkv_insert_dims.num_q_heads"]) == pkv.InsertDims.num_q_heads.offset
     assert int(got["pkv_insert_dims.cache_dtype"]) == pkv.InsertDims.cache_dtype.offset
     assert int(got["pkv_plan_info.single_launch"]) == pkv.PlanInfo.single_launch.offset
+    assert int(got["pkv_plan_info.waves_per_workgroup"]) == pkv.PlanInfo.waves_per_workgroup.offset
 
 
 BASE = dict(batch=64, num_q_heads=32, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
@@ -123,6 +125,25 @@ def test_plan_stream_k():
     assert plan(target_ctas=100)["ctas_per_split_grid"] == 100
     # batches above 256 fall back to the grid schedule
     assert plan(batch=300)["split_pages"] > 0
+
+
+def test_plan_head_grouped_workgroups():
+    # the matrix-core stream-K plan puts up to a CU's resident waves (4 for
+    # 16-bit caches, 8 for fp8; up to 8 below one wave per CU) in one
+    # workgroup, one KV head each, when the KV head count divides the wave
+    # count: a divisor of Hkv
+    assert plan()["waves_per_workgroup"] == 4
+    assert plan(kv_dtype=torch.float8_e4m3fn)["waves_per_workgroup"] == 8
+    assert plan(target_ctas=2048)["waves_per_workgroup"] == 8
+    assert plan(target_ctas=512)["waves_per_workgroup"] == 2
+    assert plan(target_ctas=64)["waves_per_workgroup"] == 8
+    assert plan(num_kv_heads=2, num_q_heads=8)["waves_per_workgroup"] == 2
+    assert plan(num_kv_heads=1, num_q_heads=4)["waves_per_workgroup"] == 1
+    assert plan(num_kv_heads=6, num_q_heads=24, target_ctas=48)["waves_per_workgroup"] == 6
+    assert plan(num_kv_heads=6, num_q_heads=24, target_ctas=768)["waves_per_workgroup"] == 3
+    assert plan(num_kv_heads=6, num_q_heads=24)["waves_per_workgroup"] == 1   # 6 does not divide 1024
+    assert plan(target_ctas=12)["waves_per_workgroup"] == 1                   # 8 does not divide 12
+    assert plan(split_pages=4)["waves_per_workgroup"] == 1                    # split grid
 
 
 def test_plan_single_launch_merge():

@@ -403,6 +403,28 @@ def test_stream_k_wave_counts(name, W):
     assert_parity(w, got, run_oracle(w, inp), f"sk/{name}/W{W}")
 
 
+@pytest.mark.parametrize("hkv, W, single", [(8, 64, False), (8, 64, True), (6, 48, False),
+                                             (6, 768, False), (2, 10, False), (8, 12, False),
+                                             (8, 40, True), (4, 2048, True)])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_stream_k_head_grouped_workgroups(hkv, W, single, kv):
+    # workgroups of several waves, one KV head each, over the KV-head-major
+    # unit order (2, 3, 4, 6 and 8 heads per workgroup and the one-wave
+    # fallback), with both merges
+    base = SMALL["gqa"] if kv == "bf16" else SMALL["fp8"]
+    w = base.replace(num_kv_heads=hkv, num_q_heads=4 * hkv, batch=5, seq_len_range=(1, 700),
+                     kv_layout="NHD")
+    inp = make(w, seed=72)
+    p = pkv.query_plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=hkv,
+                       head_dim_qk=128, head_dim_v=128, pages_per_seq=inp["page_table"].shape[1],
+                       page_size=w.page_size, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
+                       window=w.window, target_ctas=W, single_launch=single)
+    print(f"[case] head groups {kv} Hkv={hkv} waves={W} single={single}: "
+          f"{p['waves_per_workgroup']} per workgroup", flush=True)
+    got = run_gpu(w, inp, target_ctas=W, single_launch=single)
+    assert_parity(w, got, run_oracle(w, inp), f"hg/{kv}/Hkv{hkv}/W{W}")
+
+
 def test_stream_k_empty_sequences_and_split_invariance():
     w = SMALL["gqa"].replace(batch=8)
     lens = [0, 1, 15, 0, 17, 63, 1023, 0]
