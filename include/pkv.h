@@ -305,13 +305,18 @@ pkv_status pkv_head_matmul(const void* x, int64_t x_stride_m, int64_t x_stride_h
  * and, when out_lse != NULL, out_lse(n, h) = M + log(w_p + w_s).  Tokens
  * n >= num_tokens_with_prefix take the suffix alone (prefix arrays then need
  * only num_tokens_with_prefix rows).  An -inf log-sum-exp contributes
- * nothing; both -inf give zeros (and -inf).  out, prefix_out, suffix_out:
- * [N, H, D] contiguous, dtype PKV_BF16 or PKV_F16, D a multiple of 8,
- * 16-byte aligned; log-sum-exps fp32 with element (n, h) at
- * lse + n * lse_stride_n + h * lse_stride_h (e.g. [H, N]: strides 1, N).
- * One launch on `stream`. */
-pkv_status pkv_merge_attn_states(void* out, const void* prefix_out, const float* prefix_lse,
-                                 const void* suffix_out, const float* suffix_lse, float* out_lse,
+ * nothing; both -inf give zeros (and -inf).  out: [N, H, D] contiguous;
+ * prefix_out and suffix_out: element (n, h, d) at x + n * stride_n +
+ * h * stride_h + d, strides in elements, multiples of 8 (the page merges
+ * the leading v_head_dim entries of wider rows); dtype PKV_BF16 or PKV_F16
+ * for all three, D a multiple of 8, pointers 16-byte aligned.  out may be
+ * suffix_out itself when that is contiguous (strides H D, D), not any other
+ * overlap.  Log-sum-exps fp32 with element (n, h) at lse + n * lse_stride_n
+ * + h * lse_stride_h (e.g. [H, N]: strides 1, N).  One launch on `stream`. */
+pkv_status pkv_merge_attn_states(void* out, const void* prefix_out, int64_t prefix_stride_n,
+                                 int64_t prefix_stride_h, const float* prefix_lse,
+                                 const void* suffix_out, int64_t suffix_stride_n,
+                                 int64_t suffix_stride_h, const float* suffix_lse, float* out_lse,
                                  int64_t lse_stride_n, int64_t lse_stride_h, int num_tokens,
                                  int num_heads, int head_dim, int num_tokens_with_prefix,
                                  int dtype, void* stream);

@@ -118,8 +118,9 @@ def lib():
                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int, _vp]
                 L.pkv_merge_attn_states.restype = ctypes.c_int
-                L.pkv_merge_attn_states.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
-                                                    ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                i64 = ctypes.c_int64
+                L.pkv_merge_attn_states.argtypes = [_vp, _vp, i64, i64, _vp, _vp, i64, i64, _vp,
+                                                    _vp, i64, i64, ctypes.c_int, ctypes.c_int,
                                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]
                 L.pkv_cache_insert.restype = ctypes.c_int
                 L.pkv_cache_insert.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
@@ -453,20 +454,28 @@ def merge_attn_states(output, prefix_output, prefix_lse, suffix_output, suffix_l
     """Merge two attention results over disjoint key sets by their natural-log
     log-sum-exps, in place into ``output`` (one launch).
 
-    outputs [N, H, D] contiguous (bf16 or f16); log-sum-exps float32 [H, N]
-    (any strides).  Tokens at or past ``num_tokens_with_prefix`` (default N)
-    take the suffix alone.  Returns ``output``.
+    ``output`` [N, H, D] contiguous (bf16 or f16); the two results [>= rows,
+    H, D] of the same dtype with a unit last stride (e.g. the leading
+    v_head_dim entries of wider rows); log-sum-exps float32 [H, N] (any
+    strides).  Tokens at or past ``num_tokens_with_prefix`` (default N) take
+    the suffix alone.  ``output`` may be ``suffix_output`` itself when that is
+    contiguous.  Returns ``output``.
     """
     if output.device.type != "cuda":
         raise PkvError(1, "merge_attn_states runs on the GPU only")
+    if not output.is_contiguous():
+        raise PkvError(1, "output must be contiguous")
     N, H, D = output.shape
     n_pre = N if num_tokens_with_prefix is None else int(num_tokens_with_prefix)
     for name, t, rows in (("prefix_output", prefix_output, n_pre), ("suffix_output", suffix_output, N)):
         if t is None and rows == 0:
             continue
         if t is None or t.dtype != output.dtype or tuple(t.shape[1:]) != (H, D) or t.shape[0] < rows \
-                or not t.is_contiguous():
-            raise PkvError(1, f"{name} must be contiguous [>= {rows}, {H}, {D}] of output's dtype")
+                or t.stride(2) != 1:
+            raise PkvError(1, f"{name} must be [>= {rows}, {H}, {D}] of output's dtype with unit "
+                              f"last stride")
+    if suffix_output.data_ptr() == output.data_ptr() and not suffix_output.is_contiguous():
+        raise PkvError(1, "output may alias suffix_output only when that is contiguous")
     for name, t in (("prefix_lse", prefix_lse), ("suffix_lse", suffix_lse), ("output_lse", output_lse)):
         if t is not None and (t.dtype != torch.float32 or t.dim() != 2 or t.shape[0] != H):
             raise PkvError(1, f"{name} must be float32 [{H}, tokens]")
@@ -477,9 +486,11 @@ def merge_attn_states(output, prefix_output, prefix_lse, suffix_output, suffix_l
     if stream is None:
         stream = torch.cuda.current_stream(output.device).cuda_stream
     with torch.cuda.device(output.device):
+        ps = (0, 0) if prefix_output is None else (prefix_output.stride(0), prefix_output.stride(1))
         st = lib().pkv_merge_attn_states(
-            _ptr(output), _ptr(prefix_output), _ptr(prefix_lse), _ptr(suffix_output), _ptr(suffix_lse),
-            _ptr(output_lse), suffix_lse.stride(1), suffix_lse.stride(0), N, H, D, n_pre,
-            _DTYPE[output.dtype], ctypes.c_void_p(stream))
+            _ptr(output), _ptr(prefix_output), ps[0], ps[1], _ptr(prefix_lse), _ptr(suffix_output),
+            suffix_output.stride(0), suffix_output.stride(1), _ptr(suffix_lse), _ptr(output_lse),
+            suffix_lse.stride(1), suffix_lse.stride(0), N, H, D, n_pre, _DTYPE[output.dtype],
+            ctypes.c_void_p(stream))
     _check(st)
     return output

@@ -580,7 +580,8 @@ pkv_status pkv_head_matmul(const void* x, int64_t xs_m, int64_t xs_h, const void
   return PKV_OK;
 }
 
-pkv_status pkv_merge_attn_states(void* out, const void* o_p, const float* lse_p, const void* o_s,
+pkv_status pkv_merge_attn_states(void* out, const void* o_p, int64_t p_sn, int64_t p_sh,
+                                 const float* lse_p, const void* o_s, int64_t s_sn, int64_t s_sh,
                                  const float* lse_s, float* lse_out, int64_t lse_sn, int64_t lse_sh,
                                  int N, int H, int D, int n_prefix, int dtype, void* stream) {
   if (N < 0 || H < 1 || D < 8 || D % 8 || n_prefix < 0 || n_prefix > N)
@@ -591,6 +592,9 @@ pkv_status pkv_merge_attn_states(void* out, const void* o_p, const float* lse_p,
     return fail(PKV_ERR_INVALID_ARGUMENT, "merge_attn_states dtype must be float16 or bfloat16");
   if (lse_sn < 0 || lse_sh < 0)
     return fail(PKV_ERR_INVALID_ARGUMENT, "log-sum-exp strides must be non-negative");
+  if (p_sn < 0 || p_sh < 0 || s_sn < 0 || s_sh < 0 || p_sn % 8 || p_sh % 8 || s_sn % 8 || s_sh % 8)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "output strides must be non-negative multiples of 8 "
+                                          "elements");
   if (N == 0) {
     g_err.clear();
     return PKV_OK;
@@ -607,6 +611,10 @@ pkv_status pkv_merge_attn_states(void* out, const void* o_p, const float* lse_p,
   p.out = out;
   p.o_p = o_p;
   p.o_s = o_s;
+  p.p_sn = p_sn;
+  p.p_sh = p_sh;
+  p.s_sn = s_sn;
+  p.s_sh = s_sh;
   p.lse_p = lse_p;
   p.lse_s = lse_s;
   p.lse_out = lse_out;

@@ -63,24 +63,29 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
 // the unit is its first) or 2 w0 + 1 (its last); every later wave up to w1
 // has the unit first and left slot 2 w.  Units held by one wave were finished
 // by the split kernel; units with no tiles get zeros here.
-// Grid (Hkv, B, row groups of 4); wave v merges row 4 * group + v.  Lane j
-// reads the (m, l) of slot j (in groups of 64), so the max and the
-// denominator are wave reductions; the slot weights are then broadcast with
-// readlane and eight slots' partial outputs are loaded at a time.
-template <int QT>
-__global__ __launch_bounds__(256) void combine_sk_kernel(Params p) {
+// One wave per (unit, group of 64 / (DV / 8) rows): each row's DV / 8 lanes
+// hold 8 consecutive dims.  The slots are merged in chunks of 8 whose (m, l)
+// pairs and partial outputs are all loaded before any is used -- one memory
+// round trip per chunk -- with the running reference moved between chunks.
+template <int QT, int DV>
+__global__ __launch_bounds__(64) void combine_sk_kernel(Params p) {
+  constexpr int LPR = DV / 8, RPW = 64 / LPR, CH = 8;
   resolve_scales(p);
-  const int kvh = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.z * 4 + (threadIdx.x >> 6);
-  if (r >= p.R) return;
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, li = lane % LPR;
+  const int r = blockIdx.x * RPW + lane / LPR;
+  const bool row_ok = r < p.R;
+  const int rr = row_ok ? r : 0;  // lanes past the last row read row 0 and store nothing
   const SkSched S = sk_schedule(p);
   const int W = sk_waves_eff(S.T, p.sk_waves);
   int pre, n;
   sk_seq_of(S, b, &pre, &n);
-  const int64_t ob = q_row_offset(p, b, kvh, r) * p.Dv;
+  const int64_t ob = q_row_offset(p, b, kvh, rr) * DV + 8 * li;
   if (n == 0) {
-    for (int d = lane; d < p.Dv; d += 64) store_out1<QT>(p, ob + d, 0.f);
+    if (row_ok) {
+      store_out4<QT>(p, ob, 0.f, 0.f, 0.f, 0.f);
+      store_out4<QT>(p, ob + 4, 0.f, 0.f, 0.f, 0.f);
+    }
     return;
   }
   const int64_t us = sk_unit_start(S, kvh, pre), ue = us + n;
@@ -88,68 +93,70 @@ __global__ __launch_bounds__(256) void combine_sk_kernel(Params p) {
   if (w0 == w1) return;
   const int64_t slot0 = sk_wave_start(S.T, w0, W) == us ? 2 * (int64_t)w0 : 2 * (int64_t)w0 + 1;
   const int nslots = w1 - w0 + 1;
-  auto row_of = [&](int j) -> int64_t {
-    return (j == 0 ? slot0 : 2 * (int64_t)(w0 + j)) * p.R + r;
-  };
-  float sk = kNegInf;
-  if (p.sinks != nullptr) sk = p.sinks[kvh * p.G + r % p.G] * kLog2e;
-  float M = sk;
-  for (int j0 = 0; j0 < nslots; j0 += 64) {
-    const int j = j0 + lane;
-    M = fmaxf(M, j < nslots ? p.ws_ml[row_of(j)].x : kNegInf);
+  // the sink term enters once: as the starting reference with weight 1
+  float M = kNegInf, den = 0.f;
+  if (p.sinks != nullptr) {
+    M = p.sinks[kvh * p.G + rr % p.G] * kLog2e;
+    den = 1.f;
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
-  float den = p.sinks != nullptr ? exp2f(sk - M) : 0.f;
   float acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-  const int per_lane = p.Dv >> 6;  // Dv in {64, 128, 256, 512}
-  for (int j0 = 0; j0 < nslots; j0 += 64) {
-    const int j = j0 + lane;
-    float wt = 0.f, lsum = 0.f;
-    if (j < nslots) {
-      const float2 ml = p.ws_ml[row_of(j)];
-      wt = ml.x == kNegInf ? 0.f : exp2f(ml.x - M);
-      lsum = wt * ml.y;
+  for (int j0 = 0; j0 < nslots; j0 += CH) {
+    float2 ml[CH];
+    float4 v[CH][2];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      // slots past the last are read as slot0 (in bounds) and weighted 0
+      const int j = j0 + u;
+      const int64_t prow = (j >= nslots ? slot0 : j == 0 ? slot0 : 2 * (int64_t)(w0 + j)) * p.R + rr;
+      ml[u] = p.ws_ml[prow];
+      const float4* src = (const float4*)(p.ws_o + prow * DV + 8 * li);
+      v[u][0] = src[0];
+      v[u][1] = src[1];
     }
+    float Mc = M;
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) lsum += __shfl_xor(lsum, d);
-    den += lsum;
-    const int cnt = min(64, nslots - j0);
-    for (int jb = 0; jb < cnt; jb += 8) {
-      float v[8][8];
+    for (int u = 0; u < CH; ++u)
+      if (j0 + u < nslots) Mc = fmaxf(Mc, ml[u].x);
+    if (Mc == kNegInf) continue;  // nothing visible so far
+    const float scale = exp2f(M - Mc);  // 0 when M is -inf
+    den *= scale;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool ok = jb + u < cnt;
-        const float* src = p.ws_o + row_of(j0 + (ok ? jb + u : 0)) * p.Dv + lane;
+    for (int k = 0; k < 8; ++k) acc[k] *= scale;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[u][k] = (ok && k < per_lane) ? src[64 * k] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        // lanes past the last slot hold weight 0 (and their loads are zeros)
-        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), jb + u));
-#pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] += wj * v[u][k];
-      }
+    for (int u = 0; u < CH; ++u) {
+      const float wu = (j0 + u < nslots && ml[u].x != kNegInf) ? exp2f(ml[u].x - Mc) : 0.f;
+      den += wu * ml[u].y;
+      acc[0] += wu * v[u][0].x; acc[1] += wu * v[u][0].y; acc[2] += wu * v[u][0].z; acc[3] += wu * v[u][0].w;
+      acc[4] += wu * v[u][1].x; acc[5] += wu * v[u][1].y; acc[6] += wu * v[u][1].z; acc[7] += wu * v[u][1].w;
     }
+    M = Mc;
   }
+  if (!row_ok) return;
   const float inv = den > 0.f ? p.out_scale / den : 0.f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k)
-    if (k < per_lane) store_out1<QT>(p, ob + lane + 64 * k, acc[k] * inv);
+  store_out4<QT>(p, ob, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  store_out4<QT>(p, ob + 4, acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
 }
 
 hipError_t launch_combine(int q_dtype, const Params& p, hipStream_t s) {
   dim3 grid(p.R, p.Hkv, p.B);
   if (p.sk_waves > 0) {
-    if (p.Dv > 512) return hipErrorInvalidValue;
-    dim3 ugrid(p.Hkv, p.B, (p.R + 3) / 4);
-    if (q_dtype == kBF16)
-      hipLaunchKernelGGL((combine_sk_kernel<kBF16>), ugrid, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL((combine_sk_kernel<kF16>), ugrid, dim3(256), 0, s, p);
+#define PKV_COMBINE_SK(DV)                                                                   \
+  if (p.Dv == DV) {                                                                          \
+    const dim3 ugrid((p.R + 64 / (DV / 8) - 1) / (64 / (DV / 8)), p.Hkv, p.B);              \
+    if (q_dtype == kBF16)                                                                    \
+      hipLaunchKernelGGL((combine_sk_kernel<kBF16, DV>), ugrid, dim3(64), 0, s, p);          \
+    else                                                                                     \
+      hipLaunchKernelGGL((combine_sk_kernel<kF16, DV>), ugrid, dim3(64), 0, s, p);           \
+    return hipGetLastError();                                                                \
+  }
+    PKV_COMBINE_SK(64)
+    PKV_COMBINE_SK(128)
+    PKV_COMBINE_SK(256)
+    PKV_COMBINE_SK(512)
+#undef PKV_COMBINE_SK
+    return hipErrorInvalidValue;
   } else if (q_dtype == kBF16) {
     hipLaunchKernelGGL((combine_kernel<kBF16>), grid, dim3(64), 0, s, p);
   } else {

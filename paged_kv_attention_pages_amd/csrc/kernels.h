@@ -47,9 +47,10 @@ hipError_t launch_head_matmul(int dtype, const HeadMatmulParams& p, hipStream_t 
 
 // Merge of two attention results by their log-sum-exps (natural log).
 struct MergeParams {
-  void* out;                  // [N, H, D]
-  const void* o_p;            // [n_prefix, H, D] prefix results
-  const void* o_s;            // [N, H, D] suffix results
+  void* out;                  // [N, H, D] contiguous
+  const void* o_p;            // prefix results: (n, h, d) at n * p_sn + h * p_sh + d
+  const void* o_s;            // suffix results: (n, h, d) at n * s_sn + h * s_sh + d
+  int64_t p_sn, p_sh, s_sn, s_sh;
   const float* lse_p;         // element (n, h) at n * lse_sn + h * lse_sh
   const float* lse_s;
   float* lse_out;             // same layout, or null

@@ -37,8 +37,9 @@ __global__ __launch_bounds__(256) void merge_states_kernel(MergeParams p) {
   const float den = wp + ws;
   const float a = den > 0.f ? wp / den : 0.f, b = den > 0.f ? ws / den : 0.f;
   const int64_t off = (int64_t)row * p.D + d;
-  const uint4 vs = *(const uint4*)((const uint16_t*)p.o_s + off);
-  const uint4 vp = has_p ? *(const uint4*)((const uint16_t*)p.o_p + off) : make_uint4(0, 0, 0, 0);
+  const uint4 vs = *(const uint4*)((const uint16_t*)p.o_s + (int64_t)n * p.s_sn + (int64_t)h * p.s_sh + d);
+  const uint4 vp = has_p ? *(const uint4*)((const uint16_t*)p.o_p + (int64_t)n * p.p_sn + (int64_t)h * p.p_sh + d)
+                         : make_uint4(0, 0, 0, 0);
   const uint32_t sw[4] = {vs.x, vs.y, vs.z, vs.w}, pw[4] = {vp.x, vp.y, vp.z, vp.w};
   uint32_t ow[4];
 #pragma unroll

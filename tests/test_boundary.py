@@ -317,14 +317,20 @@ def test_head_matmul_rejects_strides_and_nulls():
 ])
 def test_merge_attn_states_rejects_bad_sizes(N, H, D, n_pre, dtype, msg):
     L = pkv.lib()
-    st = L.pkv_merge_attn_states(None, None, None, None, None, None, 1, N, N, H, D, n_pre, dtype, None)
+    st = L.pkv_merge_attn_states(None, None, H * D, D, None, None, H * D, D, None, None, 1, N, N, H,
+                                 D, n_pre, dtype, None)
     assert st == 1 and msg in L.pkv_last_error().decode()
 
 
-def test_merge_attn_states_nulls_and_empty():
+def _merge(lse_sn=1, p_sn=128, s_sh=64, N=4, n_pre=2):
+    return pkv.lib().pkv_merge_attn_states(None, None, p_sn, 64, None, None, 128, s_sh, None, None,
+                                           lse_sn, 4, N, 2, 64, n_pre, 1, None)
+
+
+def test_merge_attn_states_nulls_strides_and_empty():
     L = pkv.lib()
-    assert L.pkv_merge_attn_states(None, None, None, None, None, None, 1, 4, 4, 2, 64, 2, 1, None) == 1
-    assert "must not be NULL" in L.pkv_last_error().decode()
-    assert L.pkv_merge_attn_states(None, None, None, None, None, None, -1, 4, 4, 2, 64, 2, 1, None) == 1
-    assert "non-negative" in L.pkv_last_error().decode()
-    assert L.pkv_merge_attn_states(None, None, None, None, None, None, 1, 0, 0, 2, 64, 0, 1, None) == 0
+    assert _merge() == 1 and "must not be NULL" in L.pkv_last_error().decode()
+    assert _merge(lse_sn=-1) == 1 and "non-negative" in L.pkv_last_error().decode()
+    assert _merge(p_sn=12) == 1 and "multiples of 8" in L.pkv_last_error().decode()
+    assert _merge(s_sh=-8) == 1 and "multiples of 8" in L.pkv_last_error().decode()
+    assert _merge(N=0, n_pre=0) == 0

@@ -105,3 +105,28 @@ def test_merge_empty_call_is_a_noop():
     lse = torch.empty(4, 0, device=DEV)
     pkv.merge_attn_states(out, out, lse, out, lse, 0, lse)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_merge_strided_results(dtype):
+    # the page merges the leading v_head_dim (128) entries of 192-wide prefix
+    # rows and 256-wide suffix rows
+    N, H, D = 50, 16, 128
+    po, pl, so, sl = _inputs(N, H, D, dtype, seed=21)
+    g = torch.Generator().manual_seed(22)
+    pw = torch.randn(N, H, 192, generator=g).to(dtype)
+    sw = torch.randn(N, H, 256, generator=g).to(dtype)
+    pw[..., :D] = po
+    sw[..., :D] = so
+    out = torch.empty(N, H, D, dtype=dtype, device=DEV)
+    lse = torch.empty(H, N, device=DEV)
+    pkv.merge_attn_states(out, pw.to(DEV)[..., :D], pl.to(DEV), sw.to(DEV)[..., :D], sl.to(DEV), 31, lse)
+    torch.cuda.synchronize()
+    _check(out, lse, po, pl, so, sl, 31, f"merge strided {dtype}")
+
+
+def test_merge_rejects_aliasing_a_strided_suffix():
+    sw = torch.zeros(4, 2, 128, dtype=torch.bfloat16, device=DEV)
+    lse = torch.zeros(2, 4, device=DEV)
+    with pytest.raises(pkv.PkvError, match="contiguous"):
+        pkv.merge_attn_states(sw[..., :64], None, None, sw[..., :64], lse, 0)
