@@ -311,6 +311,7 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
   p.Dqk = (int)Dk;
   p.Dv = (int)Dv;
   p.ps = ps;
+  p.ps_shift = __builtin_ctz((unsigned)ps);
   p.pps = d->pages_per_seq;
   p.num_pages = d->num_pages;
   p.window = window;

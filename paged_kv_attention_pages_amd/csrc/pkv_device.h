@@ -29,6 +29,7 @@ struct Params {
   int64_t v_page, v_slot, v_head;  // element strides of the V cache
   int B, Tq, Hq, Hkv, G, R, Dqk, Dv;
   int ps, pps, num_pages, window, mask_words16;
+  int ps_shift;               // log2(ps): page sizes are powers of two
   int split_pages, max_splits;
   int sk_waves;               // > 0: stream-K schedule over that many waves
                               // (or workgroups, for the latent-cache kernel)

@@ -72,11 +72,11 @@ __device__ __forceinline__ void load_tile(const Params& p, const Stream& st, int
                                           Tile<KT, D>& T) {
   using TT = Tile<KT, D>;
   const int tok0 = t << 4;
-  const int j = tok0 / p.ps - st.pg_begin;
+  const int j = (tok0 >> p.ps_shift) - st.pg_begin;
   int page = __builtin_amdgcn_readlane(st.my_page, j & 63);
   const bool ok = t < st.tile_end && (unsigned)page < (unsigned)p.num_pages;
   page = ok ? page : 0;
-  const int slot0 = tok0 % p.ps;
+  const int slot0 = tok0 & (p.ps - 1);
   const __amdgpu_buffer_rsrc_t rk =
       make_rsrc((const uint8_t*)p.k + (int64_t)page * p.k_page * TT::ELEM, ok ? st.k_page_bytes : 0u);
   const __amdgpu_buffer_rsrc_t rv =
@@ -175,12 +175,14 @@ __device__ __forceinline__ void compute_tile(const Params& p, const SeqGeom& sg,
       A.o[j] = mfma_k16<QT>(a, pb, A.o[j]);
     }
   } else {
+    // element j of tokens 0, 1 (2, 3) into one word with one byte permute:
+    // the low (j even) or high (j odd) halves of the two tokens' words
 #pragma unroll
     for (int j = 0; j < DT; ++j) {
-      const int sh = 16 * (j & 1);
-      const uint32_t e0 = (T.v[0][j >> 1] >> sh) & 0xffffu, e1 = (T.v[1][j >> 1] >> sh) & 0xffffu;
-      const uint32_t e2 = (T.v[2][j >> 1] >> sh) & 0xffffu, e3 = (T.v[3][j >> 1] >> sh) & 0xffffu;
-      A.o[j] = mfma_k16<QT>(make_uint2(e0 | (e1 << 16), e2 | (e3 << 16)), pb, A.o[j]);
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t w01 = __builtin_amdgcn_perm(T.v[1][j >> 1], T.v[0][j >> 1], sel);
+      const uint32_t w23 = __builtin_amdgcn_perm(T.v[3][j >> 1], T.v[2][j >> 1], sel);
+      A.o[j] = mfma_k16<QT>(make_uint2(w01, w23), pb, A.o[j]);
     }
   }
 }

@@ -195,7 +195,7 @@ __device__ __forceinline__ void load_tile(const Params& p, const Piece& P, int m
                                           bool live, int t, LTile& T) {
   const int lane = threadIdx.x & 63, w = wave_id();
   const int tok16 = t * kTileTok + 16 * (w >> 2);
-  const int pg = tok16 / p.ps;
+  const int pg = tok16 >> p.ps_shift;
   const int rel = pg - pg_begin;
   int page = -1;
   if (live && rel >= 0 && rel < 64) page = __builtin_amdgcn_readlane(my_page, rel);
