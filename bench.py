@@ -142,7 +142,9 @@ def main():
         reps.append(dict(inp, k_cache=k2, v_cache=k2 if w.v_from_k else inp["v_cache"].clone()))
     kv_bytes = kv_bytes_of(w, L)
     B = L.numel()
-    out = torch.empty((B, w.q_seq_len, w.num_q_heads, w.head_dim_v), dtype=w.q_dtype, device=dev)
+    # an fp8 query's output is bfloat16
+    out_dt = torch.bfloat16 if w.q_dtype == torch.float8_e4m3fn else w.q_dtype
+    out = torch.empty((B, w.q_seq_len, w.num_q_heads, w.head_dim_v), dtype=out_dt, device=dev)
     plan = pkv.query_plan(batch=B, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                           head_dim_qk=w.head_dim_qk, head_dim_v=w.head_dim_v,
                           pages_per_seq=inp["page_table"].shape[1], page_size=w.page_size,
@@ -201,7 +203,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, inp, L, args.cpu_seconds)
 
-    dtype = {torch.bfloat16: "bf16", torch.float16: "f16"}[w.q_dtype]
+    dtype = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float8_e4m3fn: "fp8"}[w.q_dtype]
     if w.kv_dtype == torch.float8_e4m3fn:
         dtype += "+fp8kv"
     rec = {

@@ -28,7 +28,8 @@
  *   page_table [batch, pages_per_seq] int32; K and V share the table
  *   seq_lens [batch] uint32; token t of sequence b lives in page
  *            page_table[b][t / page_size], slot t % page_size
- *   out      [batch, q_seq_len, num_q_heads, head_dim_v] in q_dtype
+ *   out      [batch, q_seq_len, num_q_heads, head_dim_v] in q_dtype (bf16
+ *            for an fp8 query; e4m3fn bytes with out_fp8)
  *   sinks    [num_kv_heads, num_q_heads / num_kv_heads] fp32 or NULL
  *   mask     [batch, q_seq_len, 2 * ceil(q_seq_len / 32)] uint16 or NULL
  *
@@ -104,7 +105,9 @@ typedef struct pkv_dims {
   int32_t head_dim_v;     /* V row width = out.shape[-1]                    */
   int32_t pages_per_seq;  /* page_table.shape[-1]; max_seq_len = this*page  */
   int32_t num_pages;      /* k_cache.shape[0] (physical pages)              */
-  int32_t q_dtype;        /* pkv_dtype: PKV_F16 or PKV_BF16; out dtype too  */
+  int32_t q_dtype;        /* pkv_dtype: PKV_F16 or PKV_BF16 (out dtype too);
+                             PKV_FP8_E4M3 for the latent cache's quantised
+                             query (needs an fp8 cache; out is PKV_BF16)    */
   int32_t kv_dtype;       /* pkv_dtype: == q_dtype or PKV_FP8_E4M3          */
   uint64_t workspace_bytes; /* size of the caller's workspace buffer        */
 } pkv_dims;

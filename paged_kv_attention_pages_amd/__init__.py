@@ -146,8 +146,9 @@ def _dims(q, k_cache, page_table, head_dim_v, q_seq_len, workspace_bytes=0) -> D
     d.head_dim_v = head_dim_v
     d.pages_per_seq = page_table.shape[-1]
     d.num_pages = k_cache.shape[0]
-    if q.dtype not in (torch.float16, torch.bfloat16):
-        raise PkvError(1, f"q dtype must be float16 or bfloat16, got {q.dtype}")
+    if q.dtype not in (torch.float16, torch.bfloat16, torch.float8_e4m3fn):
+        raise PkvError(1, f"q dtype must be float16, bfloat16 or float8_e4m3fn (latent cache), "
+                          f"got {q.dtype}")
     if k_cache.dtype not in _DTYPE:
         raise PkvError(1, f"unsupported KV cache dtype {k_cache.dtype}")
     d.q_dtype = _DTYPE[q.dtype]
@@ -242,12 +243,14 @@ def _shape_checks(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_head
     if seq_lens.dtype not in (torch.int32, torch.uint32) or seq_lens.numel() != B:
         raise PkvError(1, f"seq_lens must be uint32 (or int32) [batch] or [batch, 1], got "
                           f"{seq_lens.dtype} {tuple(seq_lens.shape)}")
-    out_ok = output.dtype == q.dtype or (output.dtype in (torch.float8_e4m3fn, torch.uint8)
-                                         and k_cache.dtype in (torch.float8_e4m3fn, torch.uint8))
+    # an fp8 query's output is bfloat16 (or the fp8 cache's dtype)
+    out16 = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    out_ok = output.dtype == out16 or (output.dtype in (torch.float8_e4m3fn, torch.uint8)
+                                       and k_cache.dtype in (torch.float8_e4m3fn, torch.uint8))
     if not out_ok or output.numel() != B * q_seq_len * Hq * head_dim_v:
-        raise PkvError(1, f"output must have q's dtype (or the fp8 cache's) and batch x q_seq_len "
-                          f"x num_q_heads x head_dim_v elements, got {output.dtype} "
-                          f"{tuple(output.shape)}")
+        raise PkvError(1, f"output must have q's dtype (bfloat16 for an fp8 query, or the fp8 "
+                          f"cache's) and batch x q_seq_len x num_q_heads x head_dim_v elements, "
+                          f"got {output.dtype} {tuple(output.shape)}")
     if mask is not None and q_seq_len > 1:
         want = (B, q_seq_len, ((q_seq_len + 31) // 32) * 2)
         if mask.dtype not in (torch.uint16, torch.int16) or tuple(mask.shape) != want:

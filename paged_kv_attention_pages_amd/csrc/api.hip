@@ -97,9 +97,15 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
   if (d->head_dim_qk < 1 || d->head_dim_v < 1)
     return fail(PKV_ERR_INVALID_ARGUMENT, "head dims must be >= 1; got %d / %d", d->head_dim_qk,
                 d->head_dim_v);
-  if (d->q_dtype != PKV_F16 && d->q_dtype != PKV_BF16)
-    return fail(PKV_ERR_INVALID_ARGUMENT, "q dtype must be float16 (0) or bfloat16 (1); got %d",
+  // an fp8 query (the latent path's quantised query input) goes with an fp8
+  // cache; its output is bfloat16
+  const bool q8 = d->q_dtype == PKV_FP8_E4M3;
+  if (d->q_dtype != PKV_F16 && d->q_dtype != PKV_BF16 && !q8)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "q dtype must be float16 (0), bfloat16 (1) or "
+                                          "float8_e4m3fn (2, latent cache only); got %d",
                 d->q_dtype);
+  if (q8 && d->kv_dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "an float8_e4m3fn query needs an float8_e4m3fn KV cache");
   if (d->kv_dtype != d->q_dtype && d->kv_dtype != PKV_FP8_E4M3)
     return fail(PKV_ERR_INVALID_ARGUMENT,
                 "KV cache dtype must equal the query dtype or be float8_e4m3fn; got %d for q %d",
@@ -115,9 +121,8 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
   if (want < PKV_PATH_AUTO || want > PKV_PATH_MFMA_MLA)
     return fail(PKV_ERR_INVALID_ARGUMENT, "unknown path %d", want);
 
-  const bool std_shape = Dk == Dv && (Dk == 64 || Dk == 128 || Dk == 256) && R <= 16;
-  const bool mla_shape = Dk == 576 && Dv == 512 && aliased && R <= 64 && Tq <= 32 &&
-                         d->kv_dtype != PKV_FP8_E4M3;
+  const bool std_shape = Dk == Dv && (Dk == 64 || Dk == 128 || Dk == 256) && R <= 16 && !q8;
+  const bool mla_shape = Dk == 576 && Dv == 512 && aliased && R <= 64 && Tq <= 32;
   const bool valu_ok = std_shape && Dk == 128 && R <= 8;
   int path;
   if (want == PKV_PATH_AUTO) {
@@ -128,20 +133,20 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
                   "head dims 576/512 are supported for the latent cache only (v_cache == k_cache)");
     else
       return fail(PKV_ERR_UNSUPPORTED,
-                  "unsupported shape: head_dim_qk %d, head_dim_v %d, %d rows per KV head "
-                  "(supported: equal head dims 64/128/256 with <= 16 rows, or the 576/512 "
-                  "latent cache with <= 64 rows, 16-bit cache and q_seq_len <= 32)",
-                  Dk, Dv, R);
+                  "unsupported shape: head_dim_qk %d, head_dim_v %d, %d rows per KV head%s "
+                  "(supported: equal head dims 64/128/256 with <= 16 rows and a 16-bit query, "
+                  "or the 576/512 latent cache with <= 64 rows and q_seq_len <= 32)",
+                  Dk, Dv, R, q8 ? " with an fp8 query" : "");
   } else {
     path = want;
     if (path == PKV_PATH_MFMA && !std_shape)
-      return fail(PKV_ERR_UNSUPPORTED, "matrix-core path needs equal head dims 64/128/256 and "
-                                       "<= 16 rows per KV head");
+      return fail(PKV_ERR_UNSUPPORTED, "matrix-core path needs equal head dims 64/128/256, "
+                                       "<= 16 rows per KV head and a 16-bit query");
     if (path == PKV_PATH_VALU && !valu_ok)
       return fail(PKV_ERR_UNSUPPORTED, "vector path needs head_dim 128 and <= 8 rows per KV head");
     if (path == PKV_PATH_MFMA_MLA && !mla_shape)
       return fail(PKV_ERR_UNSUPPORTED, "latent path needs head dims 576/512, v_cache == k_cache, "
-                                       "a 16-bit cache, <= 64 rows and q_seq_len <= 32");
+                                       "<= 64 rows and q_seq_len <= 32");
   }
 
   // ---- split planning: chunks of whole pages; grid sized for the CU count
@@ -341,7 +346,7 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
   hipError_t e;
   switch (pl.path) {
     case PKV_PATH_VALU: e = pkv::launch_split_valu(d->q_dtype, d->kv_dtype, (int)Dk, p, s); break;
-    case PKV_PATH_MFMA_MLA: e = pkv::launch_split_mla(d->q_dtype, p, s); break;
+    case PKV_PATH_MFMA_MLA: e = pkv::launch_split_mla(d->q_dtype, d->kv_dtype, p, s); break;
     default: e = pkv::launch_split_mfma16(d->q_dtype, d->kv_dtype, (int)Dk, p, s); break;
   }
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "split-KV launch failed: %s", hipGetErrorString(e));
@@ -350,7 +355,8 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "event record failed: %s", hipGetErrorString(e));
   }
   if (!pl.fused) {
-    e = pkv::launch_combine(d->q_dtype, p, s);
+    // an fp8 query's output is bfloat16
+    e = pkv::launch_combine(d->q_dtype == PKV_FP8_E4M3 ? PKV_BF16 : d->q_dtype, p, s);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
   }
   g_err.clear();

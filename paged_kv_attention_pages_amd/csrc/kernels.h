@@ -13,7 +13,7 @@ hipError_t launch_split_mfma16(int q_dtype, int kv_dtype, int D, const Params& p
 
 // Split-KV decode over a latent cache: one KV head, up to 64 rows, 576-wide
 // rows whose leading 512 entries are V.
-hipError_t launch_split_mla(int q_dtype, const Params& p, hipStream_t s);
+hipError_t launch_split_mla(int q_dtype, int kv_dtype, const Params& p, hipStream_t s);
 
 // Split-KV decode on the vector ALUs, up to 8 rows per KV head.
 hipError_t launch_split_valu(int q_dtype, int kv_dtype, int D, const Params& p, hipStream_t s);

@@ -71,7 +71,9 @@ struct QRegs {
 };
 
 // This wave's share of one tile on its way to LDS: rows 4w + (lane / 16),
-// bytes 16 (lane mod 16) + 256 j (j < 4) and 1024 + 8 (lane mod 16).
+// bytes 16 (lane mod 16) + 256 j (j < 4) and 1024 + 8 (lane mod 16) of a
+// 16-bit row; of an fp8 row (576 bytes), bytes 16 (lane mod 16) + 256 j
+// (j < 2) in a[0..1] and 512 + 4 (lane mod 16) in b.x.
 struct LTile {
   uint4 a[4];
   uint2 b;
@@ -155,8 +157,10 @@ __device__ __forceinline__ LdsOff lds_offsets() {
   return o;
 }
 
+template <bool KV8>
 __device__ __forceinline__ void setup_piece(const Params& p, int b, int kvh, int tok_lo, int tok_hi,
                                             Piece& P) {
+  constexpr int E = KV8 ? 1 : 2;  // bytes per cache element
   const int lane = threadIdx.x & 63, n = lane & 15, w = wave_id();
   const SeqGeom sg = seq_geom(p, b);
   P.b = b;
@@ -167,21 +171,31 @@ __device__ __forceinline__ void setup_piece(const Params& p, int b, int kvh, int
   P.lo_last = p.window > 0 ? sg.L - p.window : INT32_MIN;
   P.mask_from = (p.Tq > 1 && p.mask != nullptr) ? sg.L - p.Tq : sg.L;
   // this lane's row inside the wave's 16-token block: 4 (w mod 4) + lane / 16
-  P.lane_row = (int)(((4 * (w & 3) + (lane >> 4)) * p.k_slot + kvh * p.k_head) * 2) + 16 * n;
-  P.page_bytes = (uint32_t)(p.k_page * 2);
+  P.lane_row = (int)(((4 * (w & 3) + (lane >> 4)) * p.k_slot + kvh * p.k_head) * E) + 16 * n;
+  P.page_bytes = (uint32_t)(p.k_page * E);
   const int own = 16 * (w & 3) + n;
   P.vis = row_vis(p, b, sg.L, own < p.R ? own : 0);
 }
 
-// This wave's slice of its 16 query rows (zeros for rows >= R).
+// This wave's slice of its 16 query rows (zeros for rows >= R); an fp8
+// query (Q8) is converted exactly to QT.
+template <int QT, bool Q8>
 __device__ __forceinline__ void load_q(const Params& p, const Piece& P, QRegs& Q) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4, w = wave_id();
   const int row = 16 * (w & 3) + n, h = w >> 2;
   const bool ok = row < p.R;
-  const uint16_t* qrow = (const uint16_t*)p.q + q_row_offset(p, P.b, P.kvh, ok ? row : 0) * kDqk;
+  const int64_t qoff = q_row_offset(p, P.b, P.kvh, ok ? row : 0) * kDqk;
 #pragma unroll
-  for (int s = 0; s < kQkSteps; ++s)
-    Q.k[s] = ok ? *(const uint4*)(qrow + kQkHalf * h + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0);
+  for (int s = 0; s < kQkSteps; ++s) {
+    const int64_t e = qoff + kQkHalf * h + 32 * s + 8 * g;
+    if constexpr (Q8) {
+      const uint2 raw = ok ? *(const uint2*)((const uint8_t*)p.q + e) : make_uint2(0, 0);
+      const uint2 lo = fp8x4_to_16<QT>(raw.x), hi = fp8x4_to_16<QT>(raw.y);
+      Q.k[s] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+      Q.k[s] = ok ? *(const uint4*)((const uint16_t*)p.q + e) : make_uint4(0, 0, 0, 0);
+    }
+  }
 }
 
 // Issue this wave's loads of tile t: rows 4w .. 4w + 3 lie in the 16-token
@@ -191,8 +205,10 @@ __device__ __forceinline__ void load_q(const Params& p, const Piece& P, QRegs& Q
 // memory access), and rows outside [tok_lo, tok_hi) get an offset past the
 // end of the page, which also reads zeros -- so the invisible rows, which
 // may hold anything, never reach the arithmetic.
+template <bool KV8>
 __device__ __forceinline__ void load_tile(const Params& p, const Piece& P, int my_page, int pg_begin,
                                           bool live, int t, LTile& T) {
+  constexpr int E = KV8 ? 1 : 2;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int tok16 = t * kTileTok + 16 * (w >> 2);
   const int pg = tok16 >> p.ps_shift;
@@ -200,28 +216,51 @@ __device__ __forceinline__ void load_tile(const Params& p, const Piece& P, int m
   int page = -1;
   if (live && rel >= 0 && rel < 64) page = __builtin_amdgcn_readlane(my_page, rel);
   const bool ok = (unsigned)page < (unsigned)p.num_pages;
-  const uint16_t* base = (const uint16_t*)p.k + (ok ? (int64_t)page * p.k_page : 0);
+  const uint8_t* base = (const uint8_t*)p.k + (ok ? (int64_t)page * p.k_page * E : 0);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, ok ? P.page_bytes : 0u);
-  const int soff = (int)((tok16 - pg * p.ps) * p.k_slot * 2);
+  const int soff = (int)((tok16 - (pg << p.ps_shift)) * p.k_slot * E);
   const int tok = tok16 + 4 * (w & 3) + (lane >> 4);
   const bool in = tok >= P.tok_lo && tok < P.tok_hi;
   const int va = in ? P.lane_row : (int)0x80000000u;
-  const int vb = in ? P.lane_row + 1024 - 8 * (lane & 15) : (int)0x80000000u;
+  if constexpr (KV8) {
+    const int vb = in ? P.lane_row + 512 - 12 * (lane & 15) : (int)0x80000000u;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) buf_load<4>(rs, va + 256 * j, soff, (uint32_t*)&T.a[j]);
-  buf_load<2>(rs, vb, soff, (uint32_t*)&T.b);
+    for (int j = 0; j < 2; ++j) buf_load<4>(rs, va + 256 * j, soff, (uint32_t*)&T.a[j]);
+    buf_load<1>(rs, vb, soff, (uint32_t*)&T.b);
+  } else {
+    const int vb = in ? P.lane_row + 1024 - 8 * (lane & 15) : (int)0x80000000u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) buf_load<4>(rs, va + 256 * j, soff, (uint32_t*)&T.a[j]);
+    buf_load<2>(rs, vb, soff, (uint32_t*)&T.b);
+  }
 }
 
-// Write this wave's rows of a tile into LDS ring slot `slot`.
+// Write this wave's rows of a tile into LDS ring slot `slot`; fp8 rows are
+// converted exactly to QT on the way (the LDS tile is 16-bit either way).
+template <int QT, bool KV8>
 __device__ __forceinline__ void store_tile(const LTile& T, int slot, Smem& sm) {
   const int lane = threadIdx.x & 63, n = lane & 15, w = wave_id();
   const int r = 4 * (w & 3) + (lane >> 4);   // row in half tile w / 4
   uint8_t* half = sm.tile[slot] + (w >> 2) * kHalfBytes;
-  // chunk n + 16 j lands at 16 j + (n ^ swz_lo(r))
-  uint8_t* lo = half + lo_chunk(r, n);
+  uint8_t* hi = half + kHiOff + r * kHiBytes + 16 * ((n >> 1) ^ swz_hi(r)) + 8 * (n & 1);
+  if constexpr (KV8) {
+    // fp8 bytes 16 n + 256 j .. + 16 are elements of 16-bit chunks 2 n + 32 j
+    // and 2 n + 32 j + 1; rope elements 4 n .. 4 n + 3 fill half a chunk
 #pragma unroll
-  for (int j = 0; j < 4; ++j) *(uint4*)(lo + 256 * j) = T.a[j];
-  *(uint2*)(half + kHiOff + r * kHiBytes + 16 * ((n >> 1) ^ swz_hi(r)) + 8 * (n & 1)) = T.b;
+    for (int j = 0; j < 2; ++j) {
+      const uint2 e0 = fp8x4_to_16<QT>(T.a[j].x), e1 = fp8x4_to_16<QT>(T.a[j].y);
+      const uint2 e2 = fp8x4_to_16<QT>(T.a[j].z), e3 = fp8x4_to_16<QT>(T.a[j].w);
+      *(uint4*)(half + lo_chunk(r, 2 * n + 32 * j)) = make_uint4(e0.x, e0.y, e1.x, e1.y);
+      *(uint4*)(half + lo_chunk(r, 2 * n + 32 * j + 1)) = make_uint4(e2.x, e2.y, e3.x, e3.y);
+    }
+    *(uint2*)hi = fp8x4_to_16<QT>(T.b.x);
+  } else {
+    // chunk n + 16 j lands at 16 j + (n ^ swz_lo(r))
+    uint8_t* lo = half + lo_chunk(r, n);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *(uint4*)(lo + 256 * j) = T.a[j];
+    *(uint2*)hi = T.b;
+  }
 }
 
 // One tile from LDS ring slot `slot`: partial scores, swap, softmax, P . V.
@@ -362,7 +401,7 @@ __device__ __forceinline__ Run open_run(const Params& p, const Piece& P, int run
 // the ring slot freed by tile t - 1 and issues the loads of tile
 // t + 2 + kLoadRing.  The register ring holds kLoadRing tiles in flight per
 // wave; the loop is unrolled by kLoadRing to index it statically.
-template <int QT>
+template <int QT, bool KV8>
 __device__ __forceinline__ void stream_piece(const Params& p, const Piece& P, const QRegs& Q, const LdsOff& L, Run R,
                                              int t_to, Smem& sm, Acc& A) {
   const int lane = threadIdx.x & 63, w = wave_id();
@@ -371,15 +410,15 @@ __device__ __forceinline__ void stream_piece(const Params& p, const Piece& P, co
     const int tb0 = R.begin, te = R.end;
     LTile lr[kLoadRing];
     LTile first[2];
-    load_tile(p, P, R.my_page, R.pg_begin, tb0 < te, tb0, first[0]);
-    load_tile(p, P, R.my_page, R.pg_begin, tb0 + 1 < te, tb0 + 1, first[1]);
+    load_tile<KV8>(p, P, R.my_page, R.pg_begin, tb0 < te, tb0, first[0]);
+    load_tile<KV8>(p, P, R.my_page, R.pg_begin, tb0 + 1 < te, tb0 + 1, first[1]);
 #pragma unroll
     for (int k = 0; k < kLoadRing; ++k)
-      load_tile(p, P, R.my_page, R.pg_begin, tb0 + 2 + k < te, tb0 + 2 + k, lr[k]);
+      load_tile<KV8>(p, P, R.my_page, R.pg_begin, tb0 + 2 + k < te, tb0 + 2 + k, lr[k]);
     // the ring may still be read by the previous run or piece
     lds_barrier();
-    store_tile(first[0], 0, sm);
-    store_tile(first[1], 1, sm);
+    store_tile<QT, KV8>(first[0], 0, sm);
+    store_tile<QT, KV8>(first[1], 1, sm);
     lds_barrier();
     for (int t = tb0; t < te; t += kLoadRing) {
 #pragma unroll
@@ -399,11 +438,11 @@ __device__ __forceinline__ void stream_piece(const Params& p, const Piece& P, co
           // tile tt - 1 before it reached this step's barrier); stored after
           // this tile's work, so a late load stalls the wave only once the
           // step's matrix work is done, and still ahead of the next barrier
-          store_tile(lr[k], (i + 2) % kRing, sm);
+          store_tile<QT, KV8>(lr[k], (i + 2) % kRing, sm);
         }
         // issued on every step, live or not, so the wait counts before the
         // stores stay exact and kLoadRing tiles remain in flight
-        load_tile(p, P, R.my_page, R.pg_begin, tt + 2 + kLoadRing < te, tt + 2 + kLoadRing, lr[k]);
+        load_tile<KV8>(p, P, R.my_page, R.pg_begin, tt + 2 + kLoadRing < te, tt + 2 + kLoadRing, lr[k]);
       }
     }
     if (te >= t_to) break;
@@ -452,8 +491,9 @@ __device__ __forceinline__ void finish_piece(const Params& p, const Piece& P, Ac
 
 }  // namespace
 
-// Grid schedule: one workgroup per (split, KV head, sequence).
-template <int QT>
+// Grid schedule: one workgroup per (split, KV head, sequence).  QT: the
+// operand and output type; KV8: fp8 cache; Q8: fp8 query.
+template <int QT, bool KV8, bool Q8>
 __global__ __launch_bounds__(kThreads) void split_mla_kernel(Params p) {
   resolve_scales(p);
   __shared__ Smem sm;
@@ -464,15 +504,15 @@ __global__ __launch_bounds__(kThreads) void split_mla_kernel(Params p) {
   const int pg_end = min(pg_begin + p.split_pages, sg.p0 + sg.npages);
   const int tok_lo = max(pg_begin * p.ps, sg.lo), tok_hi = min(pg_end * p.ps, sg.L);
   Piece P;
-  setup_piece(p, b, kvh, tok_lo, tok_hi, P);
+  setup_piece<KV8>(p, b, kvh, tok_lo, tok_hi, P);
   const int t_to = (tok_hi + kTileTok - 1) >> kTileShift;
   const Run R = open_run(p, P, tok_lo >> kTileShift, t_to);
   QRegs Q;
-  load_q(p, P, Q);
+  load_q<QT, Q8>(p, P, Q);
   Acc A;
   reset(A);
   const LdsOff L = lds_offsets();
-  stream_piece<QT>(p, P, Q, L, R, t_to, sm, A);
+  stream_piece<QT, KV8>(p, P, Q, L, R, t_to, sm, A);
   finish_piece<QT>(p, P, A, sg.nsplits == 1,
                    (((int64_t)b * p.Hkv + kvh) * p.max_splits + split) * p.R);
 }
@@ -481,7 +521,7 @@ __global__ __launch_bounds__(kThreads) void split_mla_kernel(Params p) {
 // share of the tile stream of all units; units wholly inside its share are
 // finished here, the first and the last (when cut) leave partials in
 // workspace slots 2w and 2w+1.
-template <int QT>
+template <int QT, bool KV8, bool Q8>
 __global__ __launch_bounds__(kThreads) void split_mla_sk_kernel(Params p) {
   resolve_scales(p);
   __shared__ Smem sm;
@@ -531,11 +571,11 @@ __global__ __launch_bounds__(kThreads) void split_mla_sk_kernel(Params p) {
     const int tile0 = sg.lo >> kTileShift;
     const int t_from = tile0 + (x - ustart), t_to = tile0 + (seg_end - ustart);
     const int tok_lo = max(t_from * kTileTok, sg.lo), tok_hi = min(t_to * kTileTok, sg.L);
-    setup_piece(p, b, kvh, tok_lo, tok_hi, P);
+    setup_piece<KV8>(p, b, kvh, tok_lo, tok_hi, P);
     const Run R = open_run(p, P, t_from, t_to);
-    load_q(p, P, Q);
+    load_q<QT, Q8>(p, P, Q);
     reset(A);
-    stream_piece<QT>(p, P, Q, L, R, t_to, sm, A);
+    stream_piece<QT, KV8>(p, P, Q, L, R, t_to, sm, A);
     const bool complete = x == ustart && seg_end == ustart + ntiles;
     const int slot = 2 * wg + (x == x0 ? 0 : 1);
     finish_piece<QT>(p, P, A, complete, (int64_t)slot * p.R);
@@ -543,21 +583,30 @@ __global__ __launch_bounds__(kThreads) void split_mla_sk_kernel(Params p) {
   }
 }
 
-template <int QT>
+template <int QT, bool KV8, bool Q8>
 hipError_t launch_split_mla(const Params& p, hipStream_t stream) {
   if (p.sk_waves > 0) {
     if (p.sk_shift != kTileShift || p.B > kSkMaxBatch) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((split_mla_sk_kernel<QT>), dim3(p.sk_waves), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((split_mla_sk_kernel<QT, KV8, Q8>), dim3(p.sk_waves), dim3(kThreads), 0, stream, p);
   } else {
     dim3 grid(p.max_splits, p.Hkv, p.B);
-    hipLaunchKernelGGL((split_mla_kernel<QT>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((split_mla_kernel<QT, KV8, Q8>), grid, dim3(kThreads), 0, stream, p);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_split_mla(int q_dtype, const Params& p, hipStream_t s) {
-  if (q_dtype == kBF16) return launch_split_mla<kBF16>(p, s);
-  if (q_dtype == kF16) return launch_split_mla<kF16>(p, s);
+// 16-bit query and cache; 16-bit query and fp8 cache; fp8 query and cache
+// (bf16 operands and output).
+hipError_t launch_split_mla(int q_dtype, int kv_dtype, const Params& p, hipStream_t s) {
+  if (kv_dtype == kFP8) {
+    if (q_dtype == kFP8) return launch_split_mla<kBF16, true, true>(p, s);
+    if (q_dtype == kBF16) return launch_split_mla<kBF16, true, false>(p, s);
+    if (q_dtype == kF16) return launch_split_mla<kF16, true, false>(p, s);
+    return hipErrorInvalidValue;
+  }
+  if (q_dtype != kv_dtype) return hipErrorInvalidValue;
+  if (q_dtype == kBF16) return launch_split_mla<kBF16, false, false>(p, s);
+  if (q_dtype == kF16) return launch_split_mla<kF16, false, false>(p, s);
   return hipErrorInvalidValue;
 }
 

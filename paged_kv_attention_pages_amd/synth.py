@@ -82,6 +82,12 @@ WORKLOADS = {
         head_dim_v=512, q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16, kv_layout="NHD",
         page_size=64, seq_len_range=(4096, 16384), q_scale=math.sqrt(576.0 / 192.0),
         v_from_k=True),
+    # the latent path's fp8 form: e4m3fn cache (kv_scale 0.05) and e4m3fn query
+    "mla_fp8": Workload(
+        name="mla_fp8", batch=32, num_q_heads=64, num_kv_heads=1, head_dim_qk=576,
+        head_dim_v=512, q_dtype=torch.float8_e4m3fn, kv_dtype=torch.float8_e4m3fn,
+        kv_layout="NHD", page_size=64, seq_len_range=(4096, 16384),
+        q_scale=math.sqrt(576.0 / 192.0), kv_scale=0.05, kv_gen_scale=1.0 / 0.05, v_from_k=True),
 }
 
 # the order the workloads are listed in the specification of the benchmark

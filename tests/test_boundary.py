@@ -127,6 +127,14 @@ def test_plan_stream_k():
     assert plan(batch=300)["split_pages"] > 0
 
 
+def test_plan_latent_fp8_cache_and_query():
+    # the latent path takes an e4m3fn cache with a 16-bit or e4m3fn query
+    lat = dict(head_dim_qk=576, head_dim_v=512, num_kv_heads=1, num_q_heads=64)
+    for q in (torch.bfloat16, torch.float16, torch.float8_e4m3fn):
+        p = plan(q_dtype=q, kv_dtype=torch.float8_e4m3fn, **lat)
+        assert p["path"] == 3 and p["ctas_per_split_grid"] == 256
+
+
 def test_plan_head_grouped_workgroups():
     # the matrix-core stream-K plan puts up to a CU's resident waves (4 for
     # 16-bit caches, 8 for fp8; up to 8 below one wave per CU) in one
@@ -189,7 +197,8 @@ def test_plan_split_sizes_multiple_of_pages_and_at_least_256_tokens():
     (dict(window=-1), 1, "window"),
     (dict(q_seq_len=0), 1, "q_seq_len"),
     (dict(head_dim_qk=96, head_dim_v=96), 2, "unsupported shape"),
-    (dict(head_dim_qk=576, head_dim_v=512, num_kv_heads=1, num_q_heads=64, kv_dtype=torch.float8_e4m3fn), 2, ""),
+    (dict(q_dtype=torch.float8_e4m3fn, kv_dtype=torch.bfloat16), 1, "float8_e4m3fn KV cache"),
+    (dict(q_dtype=torch.float8_e4m3fn, kv_dtype=torch.float8_e4m3fn), 2, "fp8 query"),
     (dict(q_seq_len=5), 2, "rows"),
     (dict(path="valu", q_seq_len=4), 2, "vector path"),
     (dict(path="mfma_mla"), 2, "latent path"),

@@ -666,3 +666,19 @@ def test_merge_special_cases():
     both, lse2 = oracle.merge_attn_states(po, torch.full_like(sl, float("-inf")), so,
                                           torch.full_like(sl, float("-inf")))
     assert torch.equal(both, torch.zeros_like(both)) and torch.isinf(lse2).all()
+
+
+
+def test_fp8_query_equals_its_bf16_image():
+    # e4m3fn values are exact in bf16, so a query given as e4m3fn bytes gives
+    # the same attention as its bf16 image (the oracle decodes both exactly)
+    w = synth.WORKLOADS["mla"].replace(batch=2, seq_len_range=(1, 80),
+                                       kv_dtype=torch.float8_e4m3fn, kv_scale=0.05,
+                                       kv_gen_scale=20.0, q_dtype=torch.float8_e4m3fn)
+    inp = synth.make_inputs(w, 5)
+    a = oracle.decode(inp["q"], inp["k_cache"], None, inp["page_table"], inp["seq_lens"],
+                      head_dim_v=512, v_from_k=True, **synth.decode_kwargs(w))
+    b = oracle.decode(inp["q"].to(torch.bfloat16), inp["k_cache"], None, inp["page_table"],
+                      inp["seq_lens"], head_dim_v=512, v_from_k=True, **synth.decode_kwargs(w))
+    assert torch.equal(a, b)
+    assert torch.isfinite(a).all() and a.abs().max() > 0

@@ -41,10 +41,15 @@ def make(w, seed, seq_lens=None):
     return synth.make_inputs(w, seed, DEV, seq_lens=L, keep_from=keep_from(w, L))
 
 
+def out_dtype(w):
+    """The output dtype: q's, bfloat16 for an fp8 query."""
+    return torch.bfloat16 if w.q_dtype == torch.float8_e4m3fn else w.q_dtype
+
+
 def run_gpu(w, inp, **kw):
     B = inp["q"].shape[0]
     out = torch.full((B, w.q_seq_len, w.num_q_heads, w.head_dim_v), float("nan"),
-                     dtype=w.q_dtype, device=DEV)
+                     dtype=out_dtype(w), device=DEV)
     pkv.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"], inp["seq_lens"],
                     out, num_kv_heads=w.num_kv_heads, page_size=w.page_size, sinks=inp["sinks"],
                     q_scale=w.q_scale, kv_scale=w.kv_scale, sliding_win_size=w.window,
@@ -90,7 +95,7 @@ def assert_parity(w, got, ref, label=""):
     assert not torch.isnan(got).any(), f"{label}: NaN in output (unwritten or poisoned)"
     tol = tol_for(w)
     d = (got - ref).abs()
-    allowed = torch.clamp(out_half_ulp(ref, w.q_dtype) + 0.5 * tol, min=tol)
+    allowed = torch.clamp(out_half_ulp(ref, out_dtype(w)) + 0.5 * tol, min=tol)
     err = d.max().item()
     at = ref.flatten()[d.flatten().argmax()].item()
     rms = ref.pow(2).mean().sqrt().item()
@@ -571,6 +576,52 @@ def test_mla_empty_and_ragged_sequences():
         for b in (0, 5):
             assert torch.equal(got[b].float().cpu(), torch.zeros_like(got[b].float().cpu()))
         assert_parity(w, got, ref, f"mla-ragged/split{split}/W{W}")
+
+
+MLA_FP8 = MLA_SMALL.replace(kv_dtype=torch.float8_e4m3fn, kv_scale=0.05, kv_gen_scale=1.0 / 0.05)
+
+
+@pytest.mark.parametrize("q", ["bf16", "f16", "fp8"])
+@pytest.mark.parametrize("ps", [16, 64])
+@pytest.mark.parametrize("split", [0, 3])
+def test_mla_fp8_cache(q, ps, split):
+    # an e4m3fn latent cache (converted exactly to the operand type as tiles
+    # enter LDS), with a 16-bit query or the quantised (e4m3fn) query of the
+    # latent path, whose output is bfloat16
+    qd = {"bf16": torch.bfloat16, "f16": torch.float16, "fp8": torch.float8_e4m3fn}[q]
+    w = MLA_FP8.replace(q_dtype=qd, page_size=ps)
+    print(f"[case] mla fp8 cache, q {q}, ps={ps} split={split}", flush=True)
+    inp = make(w, seed=98 + ps)
+    got = run_gpu(w, inp, split_pages=split)
+    assert got.dtype == out_dtype(w)
+    assert_parity(w, got, run_oracle(w, inp), f"mla-fp8/q{q}/ps{ps}/split{split}")
+
+
+@pytest.mark.parametrize("variant", ["window_sinks_q8", "spec4_q8", "ragged_q8", "W7_q16"])
+def test_mla_fp8_variants(variant):
+    base = MLA_FP8.replace(q_dtype=torch.float8_e4m3fn)
+    kw, lens = {}, None
+    if variant == "window_sinks_q8":
+        w = base.replace(window=100, sinks=True, seq_len_range=(1, 900), q_scale=1.3)
+    elif variant == "spec4_q8":
+        w = base.replace(num_q_heads=16, q_seq_len=4, mask="causal", seq_len_range=(4, 700))
+    elif variant == "ragged_q8":
+        w = base.replace(batch=9)
+        lens = [0, 1, 31, 32, 33, 0, 64, 65, 700]
+    else:
+        w = MLA_FP8
+        kw = dict(target_ctas=7)
+    print(f"[case] mla fp8 {variant}", flush=True)
+    inp = make(w, seed=99, seq_lens=lens)
+    got = run_gpu(w, inp, **kw)
+    assert_parity(w, got, run_oracle(w, inp), f"mla-fp8/{variant}")
+
+
+def test_mla_fp8_query_rejected_off_the_latent_path():
+    w = SMALL["fp8"].replace(q_dtype=torch.float8_e4m3fn)
+    inp = make(w, seed=100)
+    with pytest.raises(pkv.PkvError, match="fp8 query|16-bit query"):
+        run_gpu(w, inp)
 
 
 @pytest.mark.parametrize("W", [1, 3, 7, 64, 5000])
