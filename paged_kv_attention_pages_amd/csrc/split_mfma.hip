@@ -511,6 +511,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int W1 = p.sk_waves / p.Hkv, hg = blockIdx.x / W1, j = blockIdx.x - hg * W1;
     w = (hg * p.sk_hb + (int)(threadIdx.x >> 6)) * W1 + j;
   }
+  // the wave index is uniform across the wave; saying so keeps the schedule,
+  // the tile indices and the buffer resources built from them in scalar
+  // registers (a value derived from threadIdx counts as per-lane, and a
+  // per-lane buffer resource costs a loop around every load)
+  w = __builtin_amdgcn_readfirstlane(w);
   if (w >= W) return;
   const int64_t x0 = sk_wave_start(S.T, w, W), x1 = sk_wave_start(S.T, w + 1, W);
   if (FUSED) zero_empty_units(p, S, w, W);
