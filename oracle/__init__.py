@@ -278,3 +278,51 @@ def merge_attn_states(prefix_out, prefix_lse, suffix_out, suffix_lse, num_tokens
             out[n, h] = acc / (wp + ws)
             lse[h, n] = M + math.log(wp + ws)
     return out, lse
+
+
+def ragged_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, *, sm_scale, causal):
+    """fp64 attention over a ragged (non-paged) batch, with its log-sum-exp.
+
+    FlashInfer `trtllm_ragged_attention_deepseek` call of the vllm-omni TRTLLM
+    backend (`cum_seq_lens_q` / `cum_seq_lens_kv`, `is_causal`, `bmm1_scale`
+    as the softmax scale), and the vLLM Kimi-K3 MLA page's chunked prefill,
+    whose `run_prefill_new_tokens` and `_compute_prefill_context` return the
+    (output, lse) pairs that `merge_attn_states` combines.
+
+    Sequence s owns query rows [cu_q[s], cu_q[s+1]) and key/value rows
+    [cu_k[s], cu_k[s+1]).  Query head h reads KV head h // (Hq / Hkv).  With
+    Lq, Lk the two lengths, query i (0-based in its sequence) sees key j iff
+    j < Lk and, when causal, j <= i + Lk - Lq (the queries are the last Lq
+    positions of the key sequence).  logit = sm_scale * q . k; out = softmax
+    weighted mean of the visible V rows; lse = natural log of the sum of
+    e^logit.  A row that sees nothing gets zeros and lse = -inf.
+
+    q [Nq, Hq, Dqk], k [Nk, Hkv, Dqk], v [Nk, Hkv, Dv].  Returns
+    (out fp64 [Nq, Hq, Dv], lse fp64 [Hq, Nq]).
+    """
+    qd = q.detach().to("cpu", torch.float64)
+    kd = k.detach().to("cpu", torch.float64)
+    vd = v.detach().to("cpu", torch.float64)
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    Nq, Hq, _ = qd.shape
+    Hkv, Dv = kd.shape[1], vd.shape[2]
+    G = Hq // Hkv
+    out = torch.zeros(Nq, Hq, Dv, dtype=torch.float64)
+    lse = torch.full((Hq, Nq), float("-inf"), dtype=torch.float64)
+    for s in range(len(cq) - 1):
+        Lq, Lk = cq[s + 1] - cq[s], ck[s + 1] - ck[s]
+        for h in range(Hq):
+            kh = kd[ck[s]:ck[s + 1], h // G]              # [Lk, Dqk]
+            vh = vd[ck[s]:ck[s + 1], h // G]              # [Lk, Dv]
+            for i in range(Lq):
+                n = Lk if not causal else max(0, min(Lk, i + Lk - Lq + 1))
+                if n == 0:
+                    continue
+                logits = sm_scale * (kh[:n] @ qd[cq[s] + i, h])
+                m = float(logits.max())
+                e = torch.exp(logits - m)
+                den = float(e.sum())
+                out[cq[s] + i, h] = (e @ vh[:n]) / den
+                lse[h, cq[s] + i] = m + math.log(den)
+    return out, lse

@@ -10,7 +10,11 @@
   causal-mask rows == shorter single-token decodes, all-ones mask == no mask;
 - the mask bit order of the reading, from a fixture;
 - page-table hygiene: unused entries are never dereferenced, a visible token
-  with a bad page id is an error.
+  with a bad page id is an error;
+- ragged (prefill) attention: torch's fp64 scaled_dot_product_attention per
+  sequence (causal masks from torch.tril), the q = 0 and one-key closed forms,
+  rows that see nothing, and context + new tokens merged == causal attention
+  over both.
 """
 import math
 import os
@@ -682,3 +686,78 @@ def test_fp8_query_equals_its_bf16_image():
                       inp["seq_lens"], head_dim_v=512, v_from_k=True, **synth.decode_kwargs(w))
     assert torch.equal(a, b)
     assert torch.isfinite(a).all() and a.abs().max() > 0
+
+
+# ---------------------------------------------------------------- ragged (prefill) attention
+
+def _ragged_case(seed, lens_q, lens_k, Hq, Hkv, Dqk, Dv):
+    g = torch.Generator().manual_seed(seed)
+    cq = [0] + list(np.cumsum(lens_q))
+    ck = [0] + list(np.cumsum(lens_k))
+    q = torch.randn(cq[-1], Hq, Dqk, generator=g, dtype=torch.float64)
+    k = torch.randn(ck[-1], Hkv, Dqk, generator=g, dtype=torch.float64)
+    v = torch.randn(ck[-1], Hkv, Dv, generator=g, dtype=torch.float64)
+    return q, k, v, cq, ck
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_equals_sdpa_per_sequence(causal):
+    # torch's scaled_dot_product_attention in fp64 on each sequence, the KV
+    # heads repeated for their query heads; a causal sequence with fewer
+    # queries than keys takes the boolean mask tril(diagonal = Lk - Lq)
+    lens_q, lens_k = [5, 1, 9, 4], [5, 7, 9, 30]
+    Hq, Hkv, scale = 6, 2, 0.37
+    q, k, v, cq, ck = _ragged_case(51, lens_q, lens_k, Hq, Hkv, 24, 16)
+    out, lse = oracle.ragged_attn(q, k, v, cq, ck, sm_scale=scale, causal=causal)
+    for s in range(len(lens_q)):
+        Lq, Lk = lens_q[s], lens_k[s]
+        qs = q[cq[s]:cq[s + 1]].transpose(0, 1)                              # [Hq, Lq, D]
+        ks = k[ck[s]:ck[s + 1]].transpose(0, 1).repeat_interleave(Hq // Hkv, 0)
+        vs = v[ck[s]:ck[s + 1]].transpose(0, 1).repeat_interleave(Hq // Hkv, 0)
+        mask = torch.ones(Lq, Lk, dtype=torch.bool).tril(diagonal=Lk - Lq) if causal else None
+        ref = torch.nn.functional.scaled_dot_product_attention(qs, ks, vs, attn_mask=mask,
+                                                               scale=scale)
+        assert torch.allclose(out[cq[s]:cq[s + 1]].transpose(0, 1), ref, rtol=0, atol=1e-12)
+
+
+def test_ragged_closed_forms():
+    # q = 0: every visible key has the same weight, so lse = log(#visible)
+    # and out = the mean of the visible V rows; one key: out = v, lse = logit
+    lens_q, lens_k = [6, 1], [10, 1]
+    q, k, v, cq, ck = _ragged_case(52, lens_q, lens_k, 2, 1, 8, 4)
+    q[:6] = 0
+    out, lse = oracle.ragged_attn(q, k, v, cq, ck, sm_scale=0.5, causal=True)
+    for i in range(6):
+        n = i + 10 - 6 + 1
+        assert abs(float(lse[0, i]) - math.log(n)) < 1e-14
+        assert torch.allclose(out[i, 0], v[:n, 0].mean(0), rtol=0, atol=1e-14)
+    assert torch.equal(out[6, 1], v[10, 0])
+    assert abs(float(lse[1, 6]) - 0.5 * float(k[10, 0] @ q[6, 1])) < 1e-14
+
+
+def test_ragged_rows_that_see_nothing():
+    # causal with fewer keys than queries: query i sees j <= i + Lk - Lq, so
+    # the first Lq - Lk rows see nothing (zeros, -inf); an empty key range too
+    q, k, v, cq, ck = _ragged_case(53, [5, 3], [2, 0], 2, 2, 8, 8)
+    out, lse = oracle.ragged_attn(q, k, v, cq, ck, sm_scale=1.0, causal=True)
+    assert torch.equal(out[:3], torch.zeros_like(out[:3])) and torch.isinf(lse[:, :3]).all()
+    assert torch.isfinite(lse[:, 3:5]).all()
+    assert torch.equal(out[5:], torch.zeros_like(out[5:])) and torch.isinf(lse[:, 5:]).all()
+
+
+def test_chunked_prefill_is_context_plus_new_tokens_merged():
+    # the Kimi-K3 chunked prefill: new tokens attend the cached context
+    # (not causal) and themselves (causal); merging the two by their
+    # log-sum-exps equals causal attention of the new tokens over context +
+    # new keys (queries aligned to the end of the key sequence)
+    C, N, Hq, Hkv = 11, 7, 4, 2
+    g = torch.Generator().manual_seed(54)
+    q = torch.randn(N, Hq, 16, generator=g, dtype=torch.float64)
+    k = torch.randn(C + N, Hkv, 16, generator=g, dtype=torch.float64)
+    v = torch.randn(C + N, Hkv, 12, generator=g, dtype=torch.float64)
+    ctx_o, ctx_l = oracle.ragged_attn(q, k[:C], v[:C], [0, N], [0, C], sm_scale=0.25, causal=False)
+    new_o, new_l = oracle.ragged_attn(q, k[C:], v[C:], [0, N], [0, N], sm_scale=0.25, causal=True)
+    out, lse = oracle.merge_attn_states(ctx_o, ctx_l, new_o, new_l)
+    full_o, full_l = oracle.ragged_attn(q, k, v, [0, N], [0, C + N], sm_scale=0.25, causal=True)
+    assert torch.allclose(out, full_o, rtol=0, atol=1e-12)
+    assert torch.allclose(lse, full_l, rtol=0, atol=1e-12)
