@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 5
+#define PKV_ABI_VERSION 6
 
 typedef enum {
   PKV_OK = 0,
@@ -323,6 +323,45 @@ pkv_status pkv_merge_attn_states(void* out, const void* prefix_out, int64_t pref
                                  int64_t lse_stride_n, int64_t lse_stride_h, int num_tokens,
                                  int num_heads, int head_dim, int num_tokens_with_prefix,
                                  int dtype, void* stream);
+
+/* ---- ragged (non-paged) attention with its log-sum-exp -------------- */
+
+/* vllm-omni TRTLLM diffusion backend page, `trtllm_ragged_attention_deepseek`
+ * (queries and keys packed by `cum_seq_lens_q` / `cum_seq_lens_kv`,
+ * `is_causal`, `bmm1_scale` = the softmax scale, `max_q_len`), and the vLLM
+ * Kimi-K3 MLA page's chunked prefill, whose `run_prefill_new_tokens` and
+ * `_compute_prefill_context` return the (output, lse) pairs that
+ * `merge_attn_states` (above) combines.
+ *
+ * Sequence s < num_seqs owns query rows [cu_seqlens_q[s], cu_seqlens_q[s+1])
+ * of q [total_q, num_q_heads, head_dim_qk] and key/value rows
+ * [cu_seqlens_k[s], cu_seqlens_k[s+1]) of k [total_k, num_kv_heads,
+ * head_dim_qk] and v [total_k, num_kv_heads, head_dim_v] (all contiguous);
+ * query head h reads KV head h / (num_q_heads / num_kv_heads).  With Lq and
+ * Lk the two lengths, query i (0-based in its sequence) sees key j iff
+ * j < Lk and, when `causal`, j <= i + Lk - Lq (the queries are the last Lq
+ * positions of the key sequence; Lq == Lk is the plain causal mask).
+ *   out[row, h]  = sum_j softmax_j(sm_scale q.k_j) v_j   (out: [total_q,
+ *                  num_q_heads, head_dim_v], dtype of q)
+ *   lse(row, h)  = log sum_j e^(sm_scale q.k_j)  (natural log, fp32, element
+ *                  (row, h) at lse + row * lse_stride_n + h * lse_stride_h,
+ *                  e.g. [H, N]: strides 1, total_q; lse may be NULL)
+ * A query that sees no key gets zeros and lse = -inf.  dtype PKV_BF16 or
+ * PKV_F16 for q, k, v and out; fp32 accumulation.  (head_dim_qk,
+ * head_dim_v) in {(64, 64), (128, 128), (192, 128)}; total_k * num_kv_heads *
+ * head_dim * 2 bytes under 2 GiB; num_seqs and num_q_heads at most 65535.
+ * cu_seqlens_*: int32 device arrays of num_seqs + 1 entries, non-decreasing;
+ * sequence bounds are clamped to [0, total_*] on the device, so any values
+ * stay in bounds.  Queries past `max_q_len` in a sequence are not computed
+ * (their rows are left unwritten): max_q_len must be at least the longest
+ * Lq (the page's `max_q_len`).  Pointers 16-byte aligned (lse 4-byte).
+ * Caller-owned memory, nothing allocated; one launch on `stream`. */
+pkv_status pkv_ragged_attn(const void* q, const void* k, const void* v,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* out,
+                           float* lse, int64_t lse_stride_n, int64_t lse_stride_h, int num_seqs,
+                           int num_q_heads, int num_kv_heads, int head_dim_qk, int head_dim_v,
+                           int total_q, int total_k, int max_q_len, float sm_scale, int causal,
+                           int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ import threading
 
 import torch
 
-__all__ = ["decode_attn", "workspace_size", "query_plan", "validate_inputs", "library_path",
+__all__ = ["ragged_attn", "decode_attn", "workspace_size", "query_plan", "validate_inputs", "library_path",
            "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "PATH_MFMA_MLA", "PkvError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -122,6 +122,10 @@ def lib():
                 L.pkv_merge_attn_states.argtypes = [_vp, _vp, i64, i64, _vp, _vp, i64, i64, _vp,
                                                     _vp, i64, i64, ctypes.c_int, ctypes.c_int,
                                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]
+                ci = ctypes.c_int
+                L.pkv_ragged_attn.restype = ctypes.c_int
+                L.pkv_ragged_attn.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, i64, i64, ci, ci,
+                                              ci, ci, ci, ci, ci, ci, ctypes.c_float, ci, ci, _vp]
                 L.pkv_cache_insert.restype = ctypes.c_int
                 L.pkv_cache_insert.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
                                                _vp, _vp, _vp, _vp, ctypes.POINTER(InsertDims)]
@@ -497,3 +501,53 @@ def merge_attn_states(output, prefix_output, prefix_lse, suffix_output, suffix_l
             ctypes.c_void_p(stream))
     _check(st)
     return output
+
+
+def ragged_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, *, max_q_len, sm_scale, causal=False,
+                out=None, return_lse=False, lse=None, stream=None):
+    """Attention over a ragged (non-paged) batch, with its natural-log
+    log-sum-exp (the TRTLLM backend page's cum_seq_lens call; the Kimi-K3
+    chunked prefill's new-token and context attentions).
+
+    q [total_q, Hq, Dqk], k [total_k, Hkv, Dqk], v [total_k, Hkv, Dv]
+    (contiguous, bf16 or f16, one dtype); cu_seqlens_q / cu_seqlens_k int32
+    [num_seqs + 1] on the same device; ``max_q_len`` bounds every sequence's
+    query count (no device sync here).  Causal: query i of a sequence sees
+    keys j <= i + Lk - Lq.  Writes ``out`` [total_q, Hq, Dv] (allocated when
+    None) and, with ``return_lse`` or a given ``lse`` (float32 [Hq, total_q],
+    any strides), the log-sum-exps.  Returns out, or (out, lse).
+    """
+    if q.device.type != "cuda":
+        raise PkvError(1, "ragged_attn runs on the GPU only")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 3 or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise PkvError(1, f"{name} must be a contiguous 3-d tensor of q's dtype on q's device")
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise PkvError(1, "ragged_attn takes bfloat16 or float16")
+    total_q, Hq, Dqk = q.shape
+    total_k, Hkv, Dv = k.shape[0], k.shape[1], v.shape[2]
+    if tuple(k.shape) != (total_k, Hkv, Dqk) or tuple(v.shape[:2]) != (total_k, Hkv):
+        raise PkvError(1, "k must be [total_k, Hkv, Dqk] and v [total_k, Hkv, Dv]")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or t.dim() != 1 or t.device != q.device or not t.is_contiguous():
+            raise PkvError(1, f"{name} must be a contiguous int32 vector on q's device")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise PkvError(1, "cu_seqlens_q and cu_seqlens_k need num_seqs + 1 entries each")
+    if out is None:
+        out = torch.empty((total_q, Hq, Dv), dtype=q.dtype, device=q.device)
+    elif tuple(out.shape) != (total_q, Hq, Dv) or out.dtype != q.dtype or not out.is_contiguous():
+        raise PkvError(1, f"out must be contiguous [{total_q}, {Hq}, {Dv}] of q's dtype")
+    if lse is None and return_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, total_q)):
+        raise PkvError(1, f"lse must be float32 [{Hq}, {total_q}]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = lib().pkv_ragged_attn(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(out), _ptr(lse),
+            0 if lse is None else lse.stride(1), 0 if lse is None else lse.stride(0),
+            cu_seqlens_q.numel() - 1, Hq, Hkv, Dqk, Dv, total_q, total_k, int(max_q_len),
+            float(sm_scale), 1 if causal else 0, _DTYPE[q.dtype], ctypes.c_void_p(stream))
+    _check(st)
+    return (out, lse) if (return_lse or lse is not None) else out

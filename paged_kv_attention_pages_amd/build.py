@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["api.hip", "split_mfma.hip", "split_mla.hip", "split_valu.hip", "combine.hip",
-           "cache_insert.hip", "head_matmul.hip", "merge_states.hip"]
+           "cache_insert.hip", "head_matmul.hip", "merge_states.hip", "ragged_attn.hip"]
 LIB = os.path.join(HERE, "libpkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 

@@ -637,4 +637,68 @@ pkv_status pkv_merge_attn_states(void* out, const void* o_p, int64_t p_sn, int64
   return PKV_OK;
 }
 
+pkv_status pkv_ragged_attn(const void* q, const void* k, const void* v, const int32_t* cu_q,
+                           const int32_t* cu_k, void* out, float* lse, int64_t lse_sn,
+                           int64_t lse_sh, int num_seqs, int Hq, int Hkv, int Dqk, int Dv,
+                           int total_q, int total_k, int max_q_len, float sm_scale, int causal,
+                           int dtype, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_q_len < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "ragged_attn needs num_seqs, total_q, total_k, max_q_len "
+                                          ">= 0 and num_q_heads a multiple of num_kv_heads (got %d, "
+                                          "%d, %d, %d; %d, %d)", num_seqs, total_q, total_k,
+                max_q_len, Hq, Hkv);
+  if (!((Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128) || (Dqk == 192 && Dv == 128)))
+    return fail(PKV_ERR_UNSUPPORTED, "ragged_attn supports head dims (qk, v) = (64, 64), "
+                                     "(128, 128) and (192, 128), not (%d, %d)", Dqk, Dv);
+  if (dtype != PKV_F16 && dtype != PKV_BF16)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "ragged_attn dtype must be float16 or bfloat16");
+  if (causal != 0 && causal != 1)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
+    return fail(PKV_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+  if (lse_sn < 0 || lse_sh < 0)
+    return fail(PKV_ERR_INVALID_ARGUMENT, "log-sum-exp strides must be non-negative");
+  if (num_seqs > 65535 || Hq > 65535)
+    return fail(PKV_ERR_UNSUPPORTED, "ragged_attn: at most 65535 sequences and query heads");
+  if ((int64_t)total_k * Hkv * (Dqk > Dv ? Dqk : Dv) * 2 >= ((int64_t)1 << 31) ||
+      (int64_t)total_q * Hq * Dqk >= ((int64_t)1 << 40))
+    return fail(PKV_ERR_UNSUPPORTED, "ragged_attn: K/V tensors must be under 2 GiB");
+  if (num_seqs == 0 || max_q_len == 0 || total_q == 0) {
+    g_err.clear();
+    return PKV_OK;
+  }
+  if (!q || !out || !cu_q || !cu_k || (total_k > 0 && (!k || !v)))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "q, out, cu_seqlens_q, cu_seqlens_k (and k, v when "
+                                          "total_k > 0) must not be NULL");
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
+      misaligned(lse, 4) || misaligned(cu_q, 4) || misaligned(cu_k, 4))
+    return fail(PKV_ERR_INVALID_ARGUMENT, "q, k, v, out must be 16-byte aligned, lse and "
+                                          "cu_seqlens 4-byte aligned");
+  pkv::RaggedParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.cu_q = cu_q;
+  p.cu_k = cu_k;
+  p.out = out;
+  p.lse = lse;
+  p.lse_sn = lse_sn;
+  p.lse_sh = lse_sh;
+  p.num_seqs = num_seqs;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.Dqk = Dqk;
+  p.Dv = Dv;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  p.max_q_len = max_q_len;
+  p.causal = causal;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  const hipError_t e = pkv::launch_ragged_attn(dtype, p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "ragged_attn launch failed: %s", hipGetErrorString(e));
+  g_err.clear();
+  return PKV_OK;
+}
+
 }  // extern "C"

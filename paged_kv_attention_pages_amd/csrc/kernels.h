@@ -59,6 +59,21 @@ struct MergeParams {
 };
 hipError_t launch_merge_states(int dtype, const MergeParams& p, hipStream_t s);
 
+// Attention over a ragged (non-paged) batch with its log-sum-exp.
+struct RaggedParams {
+  const void* q;              // [total_q, Hq, Dqk]
+  const void* k;              // [total_k, Hkv, Dqk]
+  const void* v;              // [total_k, Hkv, Dv]
+  const int32_t* cu_q;        // [num_seqs + 1]
+  const int32_t* cu_k;        // [num_seqs + 1]
+  void* out;                  // [total_q, Hq, Dv]
+  float* lse;                 // element (n, h) at n * lse_sn + h * lse_sh, or null
+  int64_t lse_sn, lse_sh;
+  int num_seqs, Hq, Hkv, G, Dqk, Dv, total_q, total_k, max_q_len, causal;
+  float scale_log2;           // sm_scale * log2(e)
+};
+hipError_t launch_ragged_attn(int dtype, const RaggedParams& p, hipStream_t s);
+
 // Log-sum-exp merge of the split partials of every sequence that needed
 // more than one split (zeros for sequences with nothing visible).
 hipError_t launch_combine(int q_dtype, const Params& p, hipStream_t s);

@@ -256,3 +256,22 @@ def decode_kwargs(w: Workload) -> dict:
     return dict(num_kv_heads=w.num_kv_heads, page_size=w.page_size, kv_layout=w.kv_layout,
                 q_scale=w.q_scale, kv_scale=w.kv_scale, sliding_win_size=w.window,
                 q_seq_len=w.q_seq_len)
+
+
+def make_ragged(lens_q, lens_k, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, dtype,
+                seed, device="cpu"):
+    """Inputs of a ragged (non-paged) attention: q [sum lens_q, Hq, Dqk] and
+    k, v [sum lens_k, Hkv, D] ~ N(0, 1) in ``dtype``, and the int32 prefix sums
+    cu_seqlens_q / cu_seqlens_k [num_seqs + 1] (host copies in *_host)."""
+    dev = torch.device(device)
+    cq = [0] + [int(x) for x in np.cumsum(lens_q)] if len(lens_q) else [0]
+    ck = [0] + [int(x) for x in np.cumsum(lens_k)] if len(lens_k) else [0]
+    g = _gen(seed * 1000 + 7, dev)
+    q = torch.randn((cq[-1], num_q_heads, head_dim_qk), generator=g, device=dev).to(dtype)
+    k = torch.randn((ck[-1], num_kv_heads, head_dim_qk), generator=g, device=dev).to(dtype)
+    v = torch.randn((ck[-1], num_kv_heads, head_dim_v), generator=g, device=dev).to(dtype)
+    return {"q": q, "k": k, "v": v,
+            "cu_seqlens_q": torch.tensor(cq, dtype=torch.int32, device=dev),
+            "cu_seqlens_k": torch.tensor(ck, dtype=torch.int32, device=dev),
+            "cu_seqlens_q_host": cq, "cu_seqlens_k_host": ck,
+            "max_q_len": max([int(x) for x in lens_q], default=0)}
