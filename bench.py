@@ -122,6 +122,8 @@ def main():
         return bench_proj(args)
     if args.workload in MERGE_WORKLOADS:
         return bench_merge(args)
+    if args.workload in RAGGED_WORKLOADS:
+        return bench_ragged(args)
 
     import paged_kv_attention_pages_amd as pkv
     from paged_kv_attention_pages_amd import synth
@@ -372,6 +374,80 @@ def bench_merge(args):
                      "achieved": round(nbytes / (kern_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(nbytes / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": None, "algorithmic_bytes": nbytes,
+                     "launch_us_mean": round(kern_ms * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+# Ragged (non-paged) attention: the new-token attention of a chunked
+# prefill at the latent model's materialised head shape (qk 192 = 128 nope +
+# 64 rope, v 128), one GPU's 64-head share, 4 sequences of 4096 new tokens,
+# causal; and the context attention of 1024 new tokens over 16384 cached
+# context tokens (not causal).
+RAGGED_WORKLOADS = {
+    "ragged_prefill": dict(lens_q=[4096] * 4, lens_k=[4096] * 4, H=64, Hkv=64, Dqk=192, Dv=128,
+                           causal=True),
+    "ragged_context": dict(lens_q=[1024] * 2, lens_k=[16384] * 2, H=64, Hkv=64, Dqk=192, Dv=128,
+                           causal=False),
+}
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_ragged(args):
+    import paged_kv_attention_pages_amd as pkv
+    from paged_kv_attention_pages_amd import synth
+    cfg = RAGGED_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    H, Hkv, Dqk, Dv = cfg["H"], cfg["Hkv"], cfg["Dqk"], cfg["Dv"]
+    inp = synth.make_ragged(cfg["lens_q"], cfg["lens_k"], H, Hkv, Dqk, Dv, torch.bfloat16, 1, dev)
+    # visible (query, key) pairs per head; two products of Dqk and Dv per pair
+    pairs = 0
+    for lq, lk in zip(cfg["lens_q"], cfg["lens_k"]):
+        pairs += sum(min(lk, max(0, i + lk - lq + 1)) for i in range(lq)) if cfg["causal"] else lq * lk
+    flops = 2 * pairs * H * (Dqk + Dv)
+    out = torch.empty((inp["q"].shape[0], H, Dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((H, inp["q"].shape[0]), dtype=torch.float32, device=dev)
+
+    def call():
+        pkv.ragged_attn(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_q"], inp["cu_seqlens_k"],
+                        max_q_len=inp["max_q_len"], sm_scale=Dqk ** -0.5, causal=cfg["causal"],
+                        out=out, lse=lse)
+
+    K_, W_ = args.steps, args.warmup
+    for _ in range(W_):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K_):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K_
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K_)]
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    kern_ms = statistics.fmean(a.elapsed_time(b) for a, b in ev)
+    value = flops / (ms * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    print(f"[bench] {args.workload}: {ms * 1e3:.1f} us/call wall, evented {kern_ms * 1e3:.1f} us, "
+          f"{value:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    rec = {
+        "metric": "ragged attention TFLOP/s (visible query-key pairs) + us/call",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K_, "warmup": W_,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "us_per_call": round(ms * 1e3, 2),
+        "config": {"workload": args.workload, "seqs": len(cfg["lens_q"]), "lens_q": cfg["lens_q"][0],
+                   "lens_k": cfg["lens_k"][0], "heads": H, "kv_heads": Hkv, "head_dim_qk": Dqk,
+                   "head_dim_v": Dv, "causal": cfg["causal"], "flops_per_call": flops},
+        "roofline": {"kernel": "ragged attention (mfma)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops": flops,
                      "launch_us_mean": round(kern_ms * 1e3, 2)},
         "cpu_baseline": None,
     }

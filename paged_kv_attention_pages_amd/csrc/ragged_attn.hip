@@ -34,6 +34,11 @@ namespace {
 
 constexpr float kNegInfR = -__builtin_inff();
 constexpr float kLn2 = 0.6931471805599453f;
+// a wave takes kSub sub-blocks of 16 queries (one per MFMA column block)
+// against each K/V tile it loads; a workgroup holds four waves
+constexpr int kSub = 2;
+constexpr int kQueriesPerWave = 16 * kSub;
+constexpr int kQueriesPerWg = 4 * kQueriesPerWave;
 
 // N 32-bit words at byte offset voff + soff with the default cache policy:
 // the K/V rows of a (sequence, head) are read again by every query block.
@@ -82,25 +87,31 @@ struct RAcc {
   f32x4 o[DV / 16];
 };
 
-// One 16-key tile.  lim: this lane's row sees keys < lim; lim_lo: the
-// smallest lim of the block's rows (tiles below it need no mask); kend: one
-// past the last key any row of the block sees (V of later keys is cleared,
-// since a zero weight times a non-finite value would not be zero).
-template <int QT, int DQK, int DV>
-__device__ __forceinline__ void rcompute(float scale_log2, int lim, int lim_lo, int kend,
-                                         const uint4* qb, int g, int t, RTile<DQK, DV>& T,
-                                         RAcc<DV>& A) {
-  using TT = RTile<DQK, DV>;
-  constexpr int DT = TT::DT;
+// Keys at or past kend (one past the last key any row of the wave sees)
+// get zero V, since a zero weight times a non-finite value would not be zero.
+template <int DQK, int DV>
+__device__ __forceinline__ void clear_v_past(int kend, int g, int t, RTile<DQK, DV>& T) {
   const int tok0 = t << 4;
   if (tok0 + 16 > kend) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const bool keep = tok0 + 4 * g + kk < kend;
 #pragma unroll
-      for (int w = 0; w < TT::VW; ++w) T.v[kk][w] = keep ? T.v[kk][w] : 0u;
+      for (int w = 0; w < RTile<DQK, DV>::VW; ++w) T.v[kk][w] = keep ? T.v[kk][w] : 0u;
     }
   }
+}
+
+// One 16-key tile for one 16-query sub-block.  lim: this lane's row sees
+// keys < lim; lim_lo: the smallest lim of the sub-block's rows (tiles below
+// it need no mask).
+template <int QT, int DQK, int DV>
+__device__ __forceinline__ void rcompute(float scale_log2, int lim, int lim_lo,
+                                         const uint4* qb, int g, int t, const RTile<DQK, DV>& T,
+                                         RAcc<DV>& A) {
+  using TT = RTile<DQK, DV>;
+  constexpr int DT = TT::DT;
+  const int tok0 = t << 4;
   f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < TT::KSTEPS; ++s)
@@ -144,32 +155,52 @@ __device__ __forceinline__ void rcompute(float scale_log2, int lim, int lim_lo, 
 }  // namespace
 
 template <int QT, int DQK, int DV>
-__global__ __launch_bounds__(256) void ragged_attn_kernel(RaggedParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void ragged_attn_kernel(RaggedParams p) {
   using TT = RTile<DQK, DV>;
   constexpr int KSTEPS = TT::KSTEPS, DT = TT::DT;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int s = blockIdx.z, h = blockIdx.y, kvh = h / p.G;
+  // workgroups are dealt to the 8 XCDs round robin (id mod 8); every query
+  // block of one (sequence, head) pair gets an id of the same residue, so
+  // they share one XCD's L2 and its copy of the pair's K/V rows: XCD x takes
+  // pairs x, x + 8, ..., each pair's blocks from the last (causal: the most
+  // keys) to the first, so the cheap blocks fill the tail
+  const int wg = blockIdx.x, xcd = wg & 7, j = wg >> 3;
+  const int pair = 8 * (j / p.q_blocks) + xcd;
+  const int qblk = p.q_blocks - 1 - (j - (j / p.q_blocks) * p.q_blocks);
+  if (pair >= p.num_seqs * p.Hq) return;
+  const int s = pair / p.Hq, h = pair - s * p.Hq, kvh = h / p.G;
   // sequence bounds, clamped to the tensors so that any cu_seqlens stay in bounds
   const int q0 = min(max(p.cu_q[s], 0), p.total_q), q1 = min(max(p.cu_q[s + 1], q0), p.total_q);
   const int k0 = min(max(p.cu_k[s], 0), p.total_k), k1 = min(max(p.cu_k[s + 1], k0), p.total_k);
   const int Lq = q1 - q0, Lk = k1 - k0;
   const int Lrun = min(Lq, p.max_q_len);   // queries computed (the rest stay unwritten)
-  const int i0 = blockIdx.x * 64 + 16 * w;
+  // wave w: queries i0 .. i0 + 31, as sub-blocks b = 0, 1 of 16 rows that
+  // share every K/V tile the wave loads
+  const int i0 = qblk * kQueriesPerWg + kQueriesPerWave * w;
   if (i0 >= Lrun) return;
   const int off = p.causal ? Lk - Lq : 0;  // query i sees keys < i + 1 + off (causal)
-  const int i = i0 + n;
-  const bool row_ok = i < Lrun;
-  const int lim = p.causal ? min(Lk, max(i + 1 + off, 0)) : Lk;
-  const int lim_lo = p.causal ? min(Lk, max(i0 + 1 + off, 0)) : Lk;
-  const int kend = p.causal ? min(Lk, max(min(i0 + 16, Lrun) + off, 0)) : Lk;
-  const int nt = (kend + 15) >> 4;
-  // Q^T operand of row i (zeros past the sequence's queries)
-  uint4 qb[KSTEPS];
-  const uint16_t* qrow = (const uint16_t*)p.q + ((int64_t)(q0 + (row_ok ? i : 0)) * p.Hq + h) * DQK;
+  int lim[kSub], lim_lo[kSub];
+  bool row_ok[kSub];
 #pragma unroll
-  for (int st = 0; st < KSTEPS; ++st)
-    qb[st] = row_ok ? *(const uint4*)(qrow + (4 * st + g) * 8) : make_uint4(0, 0, 0, 0);
+  for (int b = 0; b < kSub; ++b) {
+    const int i = i0 + 16 * b + n;
+    row_ok[b] = i < Lrun;
+    lim[b] = p.causal ? min(Lk, max(i + 1 + off, 0)) : Lk;
+    lim_lo[b] = p.causal ? min(Lk, max(i0 + 16 * b + 1 + off, 0)) : Lk;
+  }
+  const int kend = p.causal ? min(Lk, max(min(i0 + kQueriesPerWave, Lrun) + off, 0)) : Lk;
+  const int nt = (kend + 15) >> 4;
+  // Q^T operands of the rows (zeros past the computed queries)
+  uint4 qb[kSub][KSTEPS];
+#pragma unroll
+  for (int b = 0; b < kSub; ++b) {
+    const uint16_t* qrow =
+        (const uint16_t*)p.q + ((int64_t)(q0 + (row_ok[b] ? i0 + 16 * b + n : 0)) * p.Hq + h) * DQK;
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st)
+      qb[b][st] = row_ok[b] ? *(const uint4*)(qrow + (4 * st + g) * 8) : make_uint4(0, 0, 0, 0);
+  }
   // resources over the sequence's rows of this KV head's K and V, bounded by
   // the end of the tensors (offsets are 32-bit: the host checks the sizes)
   const int k_tok = p.Hkv * DQK * 2, v_tok = p.Hkv * DV * 2;   // bytes per key row
@@ -180,40 +211,59 @@ __global__ __launch_bounds__(256) void ragged_attn_kernel(RaggedParams p) {
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(kb, 0u);
   const int k_lane = n * k_tok + 16 * g;
   const int v_lane = 4 * g * v_tok + DT * n * 2;
-  RAcc<DV> A;
-  A.m = kNegInfR;
-  A.l = 0.f;
+  RAcc<DV> A[kSub];
 #pragma unroll
-  for (int j = 0; j < DT; ++j) A.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < kSub; ++b) {
+    A[b].m = kNegInfR;
+    A[b].l = 0.f;
+#pragma unroll
+    for (int j = 0; j < DT; ++j) A[b].o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   TT buf[2];
   load_rtile<DQK, DV>(rk, rv, rz, 0 < nt, 0, k_lane, v_lane, k_tok, v_tok, buf[0]);
   for (int t = 0; t < nt; t += 2) {
     load_rtile<DQK, DV>(rk, rv, rz, t + 1 < nt, t + 1, k_lane, v_lane, k_tok, v_tok, buf[1]);
-    rcompute<QT, DQK, DV>(p.scale_log2, lim, lim_lo, kend, qb, g, t, buf[0], A);
+    clear_v_past<DQK, DV>(kend, g, t, buf[0]);
+#pragma unroll
+    for (int b = 0; b < kSub; ++b)
+      rcompute<QT, DQK, DV>(p.scale_log2, lim[b], lim_lo[b], qb[b], g, t, buf[0], A[b]);
     load_rtile<DQK, DV>(rk, rv, rz, t + 2 < nt, t + 2, k_lane, v_lane, k_tok, v_tok, buf[0]);
-    if (t + 1 < nt) rcompute<QT, DQK, DV>(p.scale_log2, lim, lim_lo, kend, qb, g, t + 1, buf[1], A);
+    if (t + 1 < nt) {
+      clear_v_past<DQK, DV>(kend, g, t + 1, buf[1]);
+#pragma unroll
+      for (int b = 0; b < kSub; ++b)
+        rcompute<QT, DQK, DV>(p.scale_log2, lim[b], lim_lo[b], qb[b], g, t + 1, buf[1], A[b]);
+    }
   }
-  const float l = sum_across_rows(A.l);
-  if (!row_ok) return;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  // lane (n, g) holds dims DT (4 g + ii) + j of row i
-  uint16_t* orow = (uint16_t*)p.out + ((int64_t)(q0 + i) * p.Hq + h) * DV;
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii)
+  for (int b = 0; b < kSub; ++b) {
+    const float l = sum_across_rows(A[b].l);
+    if (!row_ok[b]) continue;
+    const int i = i0 + 16 * b + n;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    // lane (n, g) holds dims DT (4 g + ii) + j of row i
+    uint16_t* orow = (uint16_t*)p.out + ((int64_t)(q0 + i) * p.Hq + h) * DV;
 #pragma unroll
-    for (int j = 0; j < DT; j += 4)
-      *(uint2*)(orow + DT * (4 * g + ii) + j) =
-          make_uint2(pack2<QT>(A.o[j][ii] * inv, A.o[j + 1][ii] * inv),
-                     pack2<QT>(A.o[j + 2][ii] * inv, A.o[j + 3][ii] * inv));
-  if (p.lse != nullptr && g == 0)
-    p.lse[(int64_t)(q0 + i) * p.lse_sn + (int64_t)h * p.lse_sh] =
-        l > 0.f ? (A.m + log2f(l)) * kLn2 : kNegInfR;
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int j = 0; j < DT; j += 4)
+        *(uint2*)(orow + DT * (4 * g + ii) + j) =
+            make_uint2(pack2<QT>(A[b].o[j][ii] * inv, A[b].o[j + 1][ii] * inv),
+                       pack2<QT>(A[b].o[j + 2][ii] * inv, A[b].o[j + 3][ii] * inv));
+    if (p.lse != nullptr && g == 0)
+      p.lse[(int64_t)(q0 + i) * p.lse_sn + (int64_t)h * p.lse_sh] =
+          l > 0.f ? (A[b].m + log2f(l)) * kLn2 : kNegInfR;
+  }
 }
 
 template <int QT, int DQK, int DV>
 static hipError_t launch_ragged(const RaggedParams& p, hipStream_t s) {
-  const dim3 grid((p.max_q_len + 63) / 64, p.Hq, p.num_seqs);
-  hipLaunchKernelGGL((ragged_attn_kernel<QT, DQK, DV>), grid, dim3(256), 0, s, p);
+  RaggedParams q = p;
+  q.q_blocks = (p.max_q_len + kQueriesPerWg - 1) / kQueriesPerWg;
+  const int64_t groups = ((int64_t)p.num_seqs * p.Hq + 7) / 8;
+  const int64_t n = 8 * groups * q.q_blocks;
+  if (n >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((ragged_attn_kernel<QT, DQK, DV>), dim3((unsigned)n), dim3(256), 0, s, q);
   return hipGetLastError();
 }
 

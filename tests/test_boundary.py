@@ -343,3 +343,34 @@ def test_merge_attn_states_nulls_strides_and_empty():
     assert _merge(p_sn=12) == 1 and "multiples of 8" in L.pkv_last_error().decode()
     assert _merge(s_sh=-8) == 1 and "multiples of 8" in L.pkv_last_error().decode()
     assert _merge(N=0, n_pre=0) == 0
+
+
+def _ragged(num_seqs=2, Hq=4, Hkv=2, Dqk=128, Dv=128, total_q=10, total_k=12, max_q_len=8,
+            sm_scale=0.1, causal=1, dtype=1, lse_sn=1, lse_sh=10):
+    return pkv.lib().pkv_ragged_attn(None, None, None, None, None, None, None, lse_sn, lse_sh,
+                                     num_seqs, Hq, Hkv, Dqk, Dv, total_q, total_k, max_q_len,
+                                     sm_scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw, status, msg", [
+    (dict(num_seqs=-1), 1, "num_seqs"),
+    (dict(Hq=6, Hkv=4), 1, "multiple of num_kv_heads"),
+    (dict(Dqk=96, Dv=96), 2, "head dims"),
+    (dict(Dqk=192, Dv=192), 2, "head dims"),
+    (dict(dtype=2), 1, "float16 or bfloat16"),
+    (dict(causal=2), 1, "causal must be 0 or 1"),
+    (dict(sm_scale=float("nan")), 1, "finite"),
+    (dict(lse_sh=-1), 1, "non-negative"),
+    (dict(num_seqs=70000), 2, "65535"),
+    (dict(total_k=1 << 22, Hkv=2, Hq=4), 2, "2 GiB"),
+    (dict(), 1, "must not be NULL"),
+])
+def test_ragged_attn_rejects_before_launch(kw, status, msg):
+    st = _ragged(**kw)
+    assert st == status and msg in pkv.lib().pkv_last_error().decode()
+
+
+def test_ragged_attn_empty_calls_do_nothing():
+    assert _ragged(num_seqs=0) == 0
+    assert _ragged(max_q_len=0) == 0
+    assert _ragged(total_q=0) == 0
