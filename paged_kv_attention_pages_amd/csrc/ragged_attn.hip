@@ -15,16 +15,12 @@
 // only j <= i + Lk - Lq: the queries are the last Lq positions of the key
 // sequence (for the new-token attention Lq == Lk, the plain causal mask).
 //
-// A workgroup of four waves takes 64 consecutive queries of one (sequence,
-// query head); wave w takes rows 16 w .. 16 w + 15, so the four waves stream
-// the same K/V rows (the later ones from cache).  Per 16-key tile, with the
-// key tokens on the M side of both products as in the decode kernels:
-//   S^T (16 keys x 16 queries) = K (16 x Dqk) . Q^T   -- 16x16x32 MFMAs
-//   O^T (Dv x 16 queries)     += V^T (Dv x 16) . P^T  -- 16x16x16 MFMAs
-// so lane l keeps query l % 16 in both results and the online softmax is
-// per lane.  K and V come from HBM straight into the operand registers with
-// 16-byte buffer loads; the next tile's loads are issued before this tile's
-// matrix work.  The output is normalised in the kernel (no split).
+// A workgroup of four waves takes 128 consecutive queries of one (sequence,
+// query head).  It loads each 32-key tile of K and V once -- 16-byte loads
+// spread over its threads, into registers and then into a two-stage LDS ring
+// -- and every wave reads its matrix operands from LDS, with the key tokens
+// on the M side of both products as in the decode kernels.  The output is
+// normalised in the kernel (no split).
 #include "kernels.h"
 #include "pkv_device.h"
 
@@ -40,46 +36,29 @@ constexpr int kSub = 2;
 constexpr int kQueriesPerWave = 16 * kSub;
 constexpr int kQueriesPerWg = 4 * kQueriesPerWave;
 
-// N 32-bit words at byte offset voff + soff with the default cache policy:
-// the K/V rows of a (sequence, head) are read again by every query block.
-template <int N>
-__device__ __forceinline__ void rbuf_load(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint32_t* w) {
-  if constexpr (N == 4) {
-    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-    w[0] = a[0]; w[1] = a[1]; w[2] = a[2]; w[3] = a[3];
-  } else {
-    static_assert(N == 2, "16-bit V rows of 64 or 128 dims");
-    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-    w[0] = a[0]; w[1] = a[1];
-  }
+typedef short rs16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) rs16x4 lds_rs16x4;
+
+// Transposed LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane
+// a + 4 j supplies the address of four 16-bit elements, and lane 4 a + e
+// receives element e of lanes a, a + 4, a + 8, a + 12, in that order.
+__device__ __forceinline__ uint2 lds_tr16(const uint8_t* addr) {
+  const rs16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_rs16x4*)(addr));
+  return __builtin_bit_cast(uint2, v);
 }
 
-template <int DQK, int DV>
-struct RTile {
-  static constexpr int KSTEPS = DQK / 32;   // 16x16x32 steps of S^T
-  static constexpr int DT = DV / 16;        // O^T tiles (V elements per lane and token)
-  static constexpr int VW = DT / 2;         // V words per lane and token (16-bit)
-  uint32_t k[KSTEPS][4];
-  uint32_t v[4][VW];
-};
-
-// The loads of 16-key tile t: lane (n, g) takes key n's 16-byte chunk
-// 4 s + g of step s, and the DT values at dims DT n .. of keys 4 g + kk.  A
-// tile past the block's last one reads through an empty resource (zeros, no
-// memory access), so every step issues the same loads.
-template <int DQK, int DV>
-__device__ __forceinline__ void load_rtile(const __amdgpu_buffer_rsrc_t& rk,
-                                           const __amdgpu_buffer_rsrc_t& rv,
-                                           const __amdgpu_buffer_rsrc_t& rz, bool live, int t,
-                                           int k_lane, int v_lane, int k_tok, int v_tok,
-                                           RTile<DQK, DV>& T) {
-  using TT = RTile<DQK, DV>;
-  const int ks = live ? (t << 4) * k_tok : 0, vs = live ? (t << 4) * v_tok : 0;
-#pragma unroll
-  for (int s = 0; s < TT::KSTEPS; ++s) rbuf_load<4>(live ? rk : rz, k_lane + 64 * s, ks, T.k[s]);
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) rbuf_load<TT::VW>(live ? rv : rz, v_lane, vs + kk * v_tok, T.v[kk]);
+// Workgroup barrier that orders LDS only (the global prefetch stays in
+// flight across it).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
+
+// 16-byte chunk c of key row r sits at chunk c ^ (r mod 8) of the row's LDS
+// slot, so the K fragment reads (16 rows, one chunk) and the transposed V
+// reads (16 rows, 32 bytes) spread over the banks.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7); }
 
 template <int DV>
 struct RAcc {
@@ -87,79 +66,32 @@ struct RAcc {
   f32x4 o[DV / 16];
 };
 
-// Keys at or past kend (one past the last key any row of the wave sees)
-// get zero V, since a zero weight times a non-finite value would not be zero.
-template <int DQK, int DV>
-__device__ __forceinline__ void clear_v_past(int kend, int g, int t, RTile<DQK, DV>& T) {
-  const int tok0 = t << 4;
-  if (tok0 + 16 > kend) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const bool keep = tok0 + 4 * g + kk < kend;
-#pragma unroll
-      for (int w = 0; w < RTile<DQK, DV>::VW; ++w) T.v[kk][w] = keep ? T.v[kk][w] : 0u;
-    }
-  }
-}
-
-// One 16-key tile for one 16-query sub-block.  lim: this lane's row sees
-// keys < lim; lim_lo: the smallest lim of the sub-block's rows (tiles below
-// it need no mask).
-template <int QT, int DQK, int DV>
-__device__ __forceinline__ void rcompute(float scale_log2, int lim, int lim_lo,
-                                         const uint4* qb, int g, int t, const RTile<DQK, DV>& T,
-                                         RAcc<DV>& A) {
-  using TT = RTile<DQK, DV>;
-  constexpr int DT = TT::DT;
-  const int tok0 = t << 4;
-  f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < TT::KSTEPS; ++s)
-    s4 = mfma_k32<QT>(make_uint4(T.k[s][0], T.k[s][1], T.k[s][2], T.k[s][3]), qb[s], s4);
-  const bool edge = tok0 + 16 > lim_lo;
-  float x[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float xi = s4[i] * scale_log2;
-    x[i] = (!edge || tok0 + 4 * g + i < lim) ? xi : kNegInfR;
-  }
-  float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  tmax = max_across_rows(tmax);
-  // the reference A.m moves only when the tile max passes it by kSlack
-  const bool bump = tmax > A.m + kSlack;
-  const float m_new = bump ? tmax : A.m;
-  const float m_ref = m_new == kNegInfR ? 0.f : m_new;
-  const float alpha = bump ? __builtin_amdgcn_exp2f(A.m - m_ref) : 1.f;
-  float pr[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
-  // the sum takes the rounded probabilities that P . V uses
-  const uint2 pb = make_uint2(pack2<QT>(pr[0], pr[1]), pack2<QT>(pr[2], pr[3]));
-  const float2 r0 = unpack2<QT>(pb.x), r1 = unpack2<QT>(pb.y);
-  A.l = A.l * alpha + ((r0.x + r0.y) + (r1.x + r1.y));
-  A.m = m_new;
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-#pragma unroll
-    for (int j = 0; j < DT; ++j) A.o[j] *= alpha;
-  }
-  // element j of keys 0, 1 (2, 3) into one word with one byte permute
-#pragma unroll
-  for (int j = 0; j < DT; ++j) {
-    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-    const uint32_t w01 = __builtin_amdgcn_perm(T.v[1][j >> 1], T.v[0][j >> 1], sel);
-    const uint32_t w23 = __builtin_amdgcn_perm(T.v[3][j >> 1], T.v[2][j >> 1], sel);
-    A.o[j] = mfma_k16<QT>(make_uint2(w01, w23), pb, A.o[j]);
-  }
-}
-
 }  // namespace
 
+// One workgroup of four waves per 128 queries of a (sequence, head): the
+// workgroup loads each 32-key tile of K and V once (16-byte loads spread over
+// its 256 threads, straight into registers, then into a two-stage LDS ring),
+// and every wave reads its matrix operands from LDS.  Wave w holds queries
+// 32 w .. 32 w + 31 as two 16-query sub-blocks.  Per tile and sub-block:
+//   S^T (2 x 16 keys x 16 queries) = K . Q^T   -- 16x16x32 MFMAs from LDS
+//   online softmax of the 32 keys per lane
+//   O^T (Dv x 16 queries) += V^T . P^T          -- 16x16x32 MFMAs, V^T by
+//                                                  transposed LDS reads
+// The MFMA contraction index 8 g + c of P.V stands for key 4 g + c of the
+// first 16-key block (c < 4) or 16 + 4 g + c - 4 of the second: the order in
+// which the lane holds its scores, and the order of the two transposed reads.
 template <int QT, int DQK, int DV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void ragged_attn_kernel(RaggedParams p) {
-  using TT = RTile<DQK, DV>;
-  constexpr int KSTEPS = TT::KSTEPS, DT = TT::DT;
-  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  constexpr int KSTEPS = DQK / 32, DT = DV / 16;
+  constexpr int KC = DQK / 8, VC = DV / 8;              // 16-byte chunks per row
+  constexpr int KROW = DQK * 2, VROW = DV * 2;          // LDS bytes per key row
+  constexpr int TK = 32;                                // keys per tile
+  constexpr int KBYTES = TK * KROW, STAGE = KBYTES + TK * VROW;
+  constexpr int KI = TK * KC / 256, NCH = TK * (KC + VC) / 256;   // chunks per thread
+  static_assert(TK * KC % 256 == 0 && TK * VC % 256 == 0, "whole K and V loads per thread");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
   // workgroups are dealt to the 8 XCDs round robin (id mod 8); every query
   // block of one (sequence, head) pair gets an id of the same residue, so
   // they share one XCD's L2 and its copy of the pair's K/V rows: XCD x takes
@@ -175,11 +107,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void r
   const int k0 = min(max(p.cu_k[s], 0), p.total_k), k1 = min(max(p.cu_k[s + 1], k0), p.total_k);
   const int Lq = q1 - q0, Lk = k1 - k0;
   const int Lrun = min(Lq, p.max_q_len);   // queries computed (the rest stay unwritten)
-  // wave w: queries i0 .. i0 + 31, as sub-blocks b = 0, 1 of 16 rows that
-  // share every K/V tile the wave loads
-  const int i0 = qblk * kQueriesPerWg + kQueriesPerWave * w;
-  if (i0 >= Lrun) return;
+  const int qwg = qblk * kQueriesPerWg;
+  if (qwg >= Lrun) return;                 // whole workgroup: no barrier is left waiting
   const int off = p.causal ? Lk - Lq : 0;  // query i sees keys < i + 1 + off (causal)
+  const int i0 = qwg + kQueriesPerWave * w;
+  const bool has_rows = i0 < Lrun;         // wave-uniform; a wave without rows still loads
   int lim[kSub], lim_lo[kSub];
   bool row_ok[kSub];
 #pragma unroll
@@ -189,8 +121,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void r
     lim[b] = p.causal ? min(Lk, max(i + 1 + off, 0)) : Lk;
     lim_lo[b] = p.causal ? min(Lk, max(i0 + 16 * b + 1 + off, 0)) : Lk;
   }
-  const int kend = p.causal ? min(Lk, max(min(i0 + kQueriesPerWave, Lrun) + off, 0)) : Lk;
-  const int nt = (kend + 15) >> 4;
+  // one past the last key the wave's (the workgroup's) rows see
+  const int kend_w = p.causal ? min(Lk, max(min(i0 + kQueriesPerWave, Lrun) + off, 0)) : Lk;
+  const int kend = p.causal ? min(Lk, max(min(qwg + kQueriesPerWg, Lrun) + off, 0)) : Lk;
+  const int nt = (kend + TK - 1) / TK;
   // Q^T operands of the rows (zeros past the computed queries)
   uint4 qb[kSub][KSTEPS];
 #pragma unroll
@@ -209,31 +143,132 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void r
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)((int64_t)(p.total_k - k0) * k_tok - kvh * DQK * 2));
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)((int64_t)(p.total_k - k0) * v_tok - kvh * DV * 2));
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(kb, 0u);
-  const int k_lane = n * k_tok + 16 * g;
-  const int v_lane = 4 * g * v_tok + DT * n * 2;
+  // this thread's chunks of a tile: i < KI are K chunks, the rest V chunks
+  int crow[NCH], cvoff[NCH], clds[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int x = tid + 256 * i;
+    if (i < KI) {
+      crow[i] = x / KC;
+      const int c = x - crow[i] * KC;
+      cvoff[i] = crow[i] * k_tok + 16 * c;
+      clds[i] = crow[i] * KROW + 16 * swz(crow[i], c);
+    } else {
+      const int y = x - TK * KC;
+      crow[i] = y / VC;
+      const int c = y - crow[i] * VC;
+      cvoff[i] = crow[i] * v_tok + 16 * c;
+      clds[i] = KBYTES + crow[i] * VROW + 16 * swz(crow[i], c);
+    }
+  }
+  uint4 stg[NCH];
+  auto gload = [&](int t) {
+    const bool live = t < nt;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int so = live ? t * TK * (i < KI ? k_tok : v_tok) : 0;
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(live ? (i < KI ? rk : rv) : rz, cvoff[i], so, 0);
+      stg[i] = make_uint4(a[0], a[1], a[2], a[3]);
+    }
+  };
+  // keys past the last one the workgroup's rows see are stored as zeros, so
+  // a zero weight never meets a non-finite value
+  auto lwrite = [&](int t) {
+    uint8_t* base = lds + (t & 1) * STAGE;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const bool keep = t * TK + crow[i] < kend;
+      *(uint4*)(base + clds[i]) = keep ? stg[i] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // per-lane LDS offsets of the operand reads
+  int koff[KSTEPS];
+#pragma unroll
+  for (int st = 0; st < KSTEPS; ++st) koff[st] = n * KROW + 16 * swz(n, 4 * st + g);
+  // transposed V read of dims 16 jd .. + 15: lane (a + 4 jj) of its group
+  // addresses key 4 g + jj (+ 16 for the second block), dims 16 jd + 4 a .. + 3
+  const int va = n & 3, vjj = n >> 2;
   RAcc<DV> A[kSub];
 #pragma unroll
   for (int b = 0; b < kSub; ++b) {
     A[b].m = kNegInfR;
     A[b].l = 0.f;
 #pragma unroll
-    for (int j = 0; j < DT; ++j) A[b].o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jd = 0; jd < DT; ++jd) A[b].o[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  TT buf[2];
-  load_rtile<DQK, DV>(rk, rv, rz, 0 < nt, 0, k_lane, v_lane, k_tok, v_tok, buf[0]);
-  for (int t = 0; t < nt; t += 2) {
-    load_rtile<DQK, DV>(rk, rv, rz, t + 1 < nt, t + 1, k_lane, v_lane, k_tok, v_tok, buf[1]);
-    clear_v_past<DQK, DV>(kend, g, t, buf[0]);
+  gload(0);
+  lwrite(0);
+  gload(1);
+  lds_sync();
+  for (int t = 0; t < nt; ++t) {
+    const uint8_t* kt = lds + (t & 1) * STAGE;
+    const uint8_t* vt = kt + KBYTES;
+    if (has_rows && t * TK < kend_w) {
+      // ---- S^T of both 16-key blocks for both sub-blocks
+      f32x4 sc[kSub][2];
 #pragma unroll
-    for (int b = 0; b < kSub; ++b)
-      rcompute<QT, DQK, DV>(p.scale_log2, lim[b], lim_lo[b], qb[b], g, t, buf[0], A[b]);
-    load_rtile<DQK, DV>(rk, rv, rz, t + 2 < nt, t + 2, k_lane, v_lane, k_tok, v_tok, buf[0]);
-    if (t + 1 < nt) {
-      clear_v_past<DQK, DV>(kend, g, t + 1, buf[1]);
+      for (int b = 0; b < kSub; ++b) sc[b][0] = sc[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int b = 0; b < kSub; ++b)
-        rcompute<QT, DQK, DV>(p.scale_log2, lim[b], lim_lo[b], qb[b], g, t + 1, buf[1], A[b]);
+      for (int st = 0; st < KSTEPS; ++st)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const uint4 kf = *(const uint4*)(kt + kb2 * 16 * KROW + koff[st]);
+#pragma unroll
+          for (int b = 0; b < kSub; ++b) sc[b][kb2] = mfma_k32<QT>(kf, qb[b][st], sc[b][kb2]);
+        }
+      // ---- online softmax per sub-block over the 32 keys (row n; keys
+      // t TK + 16 kb2 + 4 g + i)
+      uint4 pw[kSub];
+#pragma unroll
+      for (int b = 0; b < kSub; ++b) {
+        const bool edge = (t + 1) * TK > lim_lo[b];
+        float x[8];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = t * TK + 16 * kb2 + 4 * g + i;
+            const float xi = sc[b][kb2][i] * p.scale_log2;
+            x[4 * kb2 + i] = (!edge || key < lim[b]) ? xi : kNegInfR;
+          }
+        float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        tmax = max_across_rows(tmax);
+        const bool bump = tmax > A[b].m + kSlack;
+        const float m_new = bump ? tmax : A[b].m;
+        const float m_ref = m_new == kNegInfR ? 0.f : m_new;
+        const float alpha = bump ? __builtin_amdgcn_exp2f(A[b].m - m_ref) : 1.f;
+        float pr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
+        pw[b] = make_uint4(pack2<QT>(pr[0], pr[1]), pack2<QT>(pr[2], pr[3]),
+                           pack2<QT>(pr[4], pr[5]), pack2<QT>(pr[6], pr[7]));
+        const float2 r0 = unpack2<QT>(pw[b].x), r1 = unpack2<QT>(pw[b].y);
+        const float2 r2 = unpack2<QT>(pw[b].z), r3 = unpack2<QT>(pw[b].w);
+        A[b].l = A[b].l * alpha + (((r0.x + r0.y) + (r1.x + r1.y)) + ((r2.x + r2.y) + (r3.x + r3.y)));
+        A[b].m = m_new;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+          for (int jd = 0; jd < DT; ++jd) A[b].o[jd] *= alpha;
+        }
+      }
+      // ---- O^T += V^T . P^T, 16 dims at a time
+#pragma unroll
+      for (int jd = 0; jd < DT; ++jd) {
+        const int c = 2 * jd + (va >> 1), bo = 8 * (va & 1);
+        const int r0 = 4 * g + vjj, r1 = r0 + 16;
+        const uint2 v0 = lds_tr16(vt + r0 * VROW + 16 * swz(r0, c) + bo);
+        const uint2 v1 = lds_tr16(vt + r1 * VROW + 16 * swz(r1, c) + bo);
+        const uint4 vop = make_uint4(v0.x, v0.y, v1.x, v1.y);
+#pragma unroll
+        for (int b = 0; b < kSub; ++b) A[b].o[jd] = mfma_k32<QT>(vop, pw[b], A[b].o[jd]);
+      }
     }
+    // the next tile into the stage tile t - 1 used (every wave finished it
+    // before the last barrier), then the loads of the one after
+    if (t + 1 < nt) lwrite(t + 1);
+    gload(t + 2);
+    lds_sync();
   }
 #pragma unroll
   for (int b = 0; b < kSub; ++b) {
@@ -241,15 +276,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void r
     if (!row_ok[b]) continue;
     const int i = i0 + 16 * b + n;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    // lane (n, g) holds dims DT (4 g + ii) + j of row i
+    // lane (n, g) holds dims 16 jd + 4 g + ii of row i
     uint16_t* orow = (uint16_t*)p.out + ((int64_t)(q0 + i) * p.Hq + h) * DV;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-      for (int j = 0; j < DT; j += 4)
-        *(uint2*)(orow + DT * (4 * g + ii) + j) =
-            make_uint2(pack2<QT>(A[b].o[j][ii] * inv, A[b].o[j + 1][ii] * inv),
-                       pack2<QT>(A[b].o[j + 2][ii] * inv, A[b].o[j + 3][ii] * inv));
+    for (int jd = 0; jd < DT; ++jd)
+      *(uint2*)(orow + 16 * jd + 4 * g) =
+          make_uint2(pack2<QT>(A[b].o[jd][0] * inv, A[b].o[jd][1] * inv),
+                     pack2<QT>(A[b].o[jd][2] * inv, A[b].o[jd][3] * inv));
     if (p.lse != nullptr && g == 0)
       p.lse[(int64_t)(q0 + i) * p.lse_sn + (int64_t)h * p.lse_sh] =
           l > 0.f ? (A[b].m + log2f(l)) * kLn2 : kNegInfR;
