@@ -15,12 +15,13 @@
 // only j <= i + Lk - Lq: the queries are the last Lq positions of the key
 // sequence (for the new-token attention Lq == Lk, the plain causal mask).
 //
-// A workgroup of four waves takes 128 consecutive queries of one (sequence,
-// query head).  It loads each 32-key tile of K and V once -- 16-byte loads
-// spread over its threads, into registers and then into a two-stage LDS ring
-// -- and every wave reads its matrix operands from LDS, with the key tokens
-// on the M side of both products as in the decode kernels.  The output is
-// normalised in the kernel (no split).
+// A workgroup of four waves (causal calls) or eight takes 32 consecutive
+// queries per wave of one (sequence, query head).  It loads each tile of 8
+// keys per wave of K and V once -- 16-byte loads spread over its threads,
+// into registers and then into a two-stage LDS ring -- and every wave reads
+// its matrix operands from LDS, with the key tokens on the M side of both
+// products as in the decode kernels.  The output is normalised in the kernel
+// (no split).
 #include "kernels.h"
 #include "pkv_device.h"
 
@@ -34,7 +35,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 // against each K/V tile it loads; a workgroup holds four waves
 constexpr int kSub = 2;
 constexpr int kQueriesPerWave = 16 * kSub;
-constexpr int kQueriesPerWg = 4 * kQueriesPerWave;
 
 typedef short rs16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) rs16x4 lds_rs16x4;
@@ -68,8 +68,8 @@ struct RAcc {
 
 }  // namespace
 
-// One workgroup of four waves per 128 queries of a (sequence, head): the
-// workgroup loads each 32-key tile of K and V once (16-byte loads spread over
+// One workgroup of NW waves per 32 NW queries of a (sequence, head): the
+// workgroup loads each 8 NW-key tile of K and V once (16-byte loads spread over
 // its 256 threads, straight into registers, then into a two-stage LDS ring),
 // and every wave reads its matrix operands from LDS.  Wave w holds queries
 // 32 w .. 32 w + 31 as two 16-query sub-blocks.  Per tile and sub-block:
@@ -80,15 +80,16 @@ struct RAcc {
 // The MFMA contraction index 8 g + c of P.V stands for key 4 g + c of the
 // first 16-key block (c < 4) or 16 + 4 g + c - 4 of the second: the order in
 // which the lane holds its scores, and the order of the two transposed reads.
-template <int QT, int DQK, int DV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void ragged_attn_kernel(RaggedParams p) {
+template <int QT, int DQK, int DV, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void ragged_attn_kernel(RaggedParams p) {
+  constexpr int kThreadsWg = 64 * NW, kQueriesPerWg = NW * kQueriesPerWave;
   constexpr int KSTEPS = DQK / 32, DT = DV / 16;
   constexpr int KC = DQK / 8, VC = DV / 8;              // 16-byte chunks per row
   constexpr int KROW = DQK * 2, VROW = DV * 2;          // LDS bytes per key row
-  constexpr int TK = 32;                                // keys per tile
+  constexpr int TK = 8 * NW;                            // keys per tile (halves of 32)
   constexpr int KBYTES = TK * KROW, STAGE = KBYTES + TK * VROW;
-  constexpr int KI = TK * KC / 256, NCH = TK * (KC + VC) / 256;   // chunks per thread
-  static_assert(TK * KC % 256 == 0 && TK * VC % 256 == 0, "whole K and V loads per thread");
+  constexpr int KI = TK * KC / kThreadsWg, NCH = TK * (KC + VC) / kThreadsWg;  // chunks per thread
+  static_assert(TK * KC % kThreadsWg == 0 && TK * VC % kThreadsWg == 0, "whole K and V loads per thread");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void r
   int crow[NCH], cvoff[NCH], clds[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int x = tid + 256 * i;
+    const int x = tid + kThreadsWg * i;
     if (i < KI) {
       crow[i] = x / KC;
       const int c = x - crow[i] * KC;
@@ -201,9 +202,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void r
   gload(1);
   lds_sync();
   for (int t = 0; t < nt; ++t) {
-    const uint8_t* kt = lds + (t & 1) * STAGE;
-    const uint8_t* vt = kt + KBYTES;
-    if (has_rows && t * TK < kend_w) {
+#pragma unroll
+    for (int hf = 0; hf < TK / 32; ++hf) {
+    const uint8_t* kt = lds + (t & 1) * STAGE + hf * 32 * KROW;
+    const uint8_t* vt = lds + (t & 1) * STAGE + KBYTES + hf * 32 * VROW;
+    const int key0 = t * TK + 32 * hf;
+    if (has_rows && key0 < kend_w) {
       // ---- S^T of both 16-key blocks for both sub-blocks
       f32x4 sc[kSub][2];
 #pragma unroll
@@ -221,13 +225,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void r
       uint4 pw[kSub];
 #pragma unroll
       for (int b = 0; b < kSub; ++b) {
-        const bool edge = (t + 1) * TK > lim_lo[b];
+        const bool edge = key0 + 32 > lim_lo[b];
         float x[8];
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = t * TK + 16 * kb2 + 4 * g + i;
+            const int key = key0 + 16 * kb2 + 4 * g + i;
             const float xi = sc[b][kb2][i] * p.scale_log2;
             x[4 * kb2 + i] = (!edge || key < lim[b]) ? xi : kNegInfR;
           }
@@ -264,6 +268,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void r
         for (int b = 0; b < kSub; ++b) A[b].o[jd] = mfma_k32<QT>(vop, pw[b], A[b].o[jd]);
       }
     }
+    }
     // the next tile into the stage tile t - 1 used (every wave finished it
     // before the last barrier), then the loads of the one after
     if (t + 1 < nt) lwrite(t + 1);
@@ -289,14 +294,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void r
   }
 }
 
+// Causal calls run four-wave workgroups (128 queries, 32-key tiles): the
+// rows of a workgroup see different key counts and wait for each other at
+// every tile, so smaller groups idle less.  Other calls run eight waves (256
+// queries, 64-key tiles), which halves the tile loads per query.
 template <int QT, int DQK, int DV>
 static hipError_t launch_ragged(const RaggedParams& p, hipStream_t s) {
+  const int nw = p.causal ? 4 : 8;
   RaggedParams q = p;
-  q.q_blocks = (p.max_q_len + kQueriesPerWg - 1) / kQueriesPerWg;
+  q.q_blocks = (p.max_q_len + 32 * nw - 1) / (32 * nw);
   const int64_t groups = ((int64_t)p.num_seqs * p.Hq + 7) / 8;
   const int64_t n = 8 * groups * q.q_blocks;
   if (n >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((ragged_attn_kernel<QT, DQK, DV>), dim3((unsigned)n), dim3(256), 0, s, q);
+  if (nw == 4)
+    hipLaunchKernelGGL((ragged_attn_kernel<QT, DQK, DV, 4>), dim3((unsigned)n), dim3(256), 0, s, q);
+  else
+    hipLaunchKernelGGL((ragged_attn_kernel<QT, DQK, DV, 8>), dim3((unsigned)n), dim3(512), 0, s, q);
   return hipGetLastError();
 }
 
