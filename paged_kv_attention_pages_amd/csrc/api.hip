@@ -654,8 +654,8 @@ pkv_status pkv_ragged_attn(const void* q, const void* k, const void* v, const in
     return fail(PKV_ERR_INVALID_ARGUMENT, "ragged_attn dtype must be float16 or bfloat16");
   if (causal != 0 && causal != 1)
     return fail(PKV_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
-  if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
-    return fail(PKV_ERR_INVALID_ARGUMENT, "sm_scale must be finite");
+  if (!(sm_scale > 0.f) || sm_scale == __builtin_inff())
+    return fail(PKV_ERR_INVALID_ARGUMENT, "sm_scale must be positive and finite");
   if (lse_sn < 0 || lse_sh < 0)
     return fail(PKV_ERR_INVALID_ARGUMENT, "log-sum-exp strides must be non-negative");
   if (num_seqs > 65535 || Hq > 65535)

@@ -60,10 +60,15 @@ __device__ __forceinline__ void lds_sync() {
 // reads (16 rows, 32 bytes) spread over the banks.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7); }
 
+// Online-softmax state of one 16-query sub-block: the reference max (log2
+// units), the O^T accumulators, and lsum = P . ones, i.e. every element of
+// lsum holds the lane's row sum of the rounded probabilities (the matrix
+// cores add them, in the same products as the V sums).
 template <int DV>
 struct RAcc {
-  float m, l;
+  float m;
   f32x4 o[DV / 16];
+  f32x4 lsum;
 };
 
 }  // namespace
@@ -193,7 +198,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
   for (int b = 0; b < kSub; ++b) {
     A[b].m = kNegInfR;
-    A[b].l = 0.f;
+    A[b].lsum = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jd = 0; jd < DT; ++jd) A[b].o[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -226,34 +231,32 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
       for (int b = 0; b < kSub; ++b) {
         const bool edge = key0 + 32 > lim_lo[b];
+        // raw scores, masked; the scale (> 0) enters once, in the exponent
         float x[8];
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = key0 + 16 * kb2 + 4 * g + i;
-            const float xi = sc[b][kb2][i] * p.scale_log2;
-            x[4 * kb2 + i] = (!edge || key < lim[b]) ? xi : kNegInfR;
+            x[4 * kb2 + i] = (!edge || key < lim[b]) ? sc[b][kb2][i] : kNegInfR;
           }
         float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                            fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        tmax = max_across_rows(tmax);
+        tmax = max_across_rows(tmax) * p.scale_log2;
         const bool bump = tmax > A[b].m + kSlack;
         const float m_new = bump ? tmax : A[b].m;
         const float m_ref = m_new == kNegInfR ? 0.f : m_new;
         const float alpha = bump ? __builtin_amdgcn_exp2f(A[b].m - m_ref) : 1.f;
         float pr[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
+        for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], p.scale_log2, -m_ref));
         pw[b] = make_uint4(pack2<QT>(pr[0], pr[1]), pack2<QT>(pr[2], pr[3]),
                            pack2<QT>(pr[4], pr[5]), pack2<QT>(pr[6], pr[7]));
-        const float2 r0 = unpack2<QT>(pw[b].x), r1 = unpack2<QT>(pw[b].y);
-        const float2 r2 = unpack2<QT>(pw[b].z), r3 = unpack2<QT>(pw[b].w);
-        A[b].l = A[b].l * alpha + (((r0.x + r0.y) + (r1.x + r1.y)) + ((r2.x + r2.y) + (r3.x + r3.y)));
         A[b].m = m_new;
         if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
           for (int jd = 0; jd < DT; ++jd) A[b].o[jd] *= alpha;
+          A[b].lsum *= alpha;
         }
       }
       // ---- O^T += V^T . P^T, 16 dims at a time
@@ -267,6 +270,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
         for (int b = 0; b < kSub; ++b) A[b].o[jd] = mfma_k32<QT>(vop, pw[b], A[b].o[jd]);
       }
+      // the row sums: P . ones (1.0 in the operand type)
+      const uint32_t one2 = QT == kBF16 ? 0x3f803f80u : 0x3c003c00u;
+#pragma unroll
+      for (int b = 0; b < kSub; ++b)
+        A[b].lsum = mfma_k32<QT>(make_uint4(one2, one2, one2, one2), pw[b], A[b].lsum);
     }
     }
     // the next tile into the stage tile t - 1 used (every wave finished it
@@ -277,7 +285,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 #pragma unroll
   for (int b = 0; b < kSub; ++b) {
-    const float l = sum_across_rows(A[b].l);
+    const float l = A[b].lsum[0];
     if (!row_ok[b]) continue;
     const int i = i0 + 16 * b + n;
     const float inv = l > 0.f ? 1.f / l : 0.f;

@@ -360,6 +360,8 @@ def _ragged(num_seqs=2, Hq=4, Hkv=2, Dqk=128, Dv=128, total_q=10, total_k=12, ma
     (dict(dtype=2), 1, "float16 or bfloat16"),
     (dict(causal=2), 1, "causal must be 0 or 1"),
     (dict(sm_scale=float("nan")), 1, "finite"),
+    (dict(sm_scale=0.0), 1, "positive"),
+    (dict(sm_scale=-0.5), 1, "positive"),
     (dict(lse_sh=-1), 1, "non-negative"),
     (dict(num_seqs=70000), 2, "65535"),
     (dict(total_k=1 << 22, Hkv=2, Hq=4), 2, "2 GiB"),
