@@ -93,7 +93,8 @@ struct Piece {
 
 struct Acc {
   f32x4 o[16];     // [m][i]: dims 256 h + 16 m + 4 g + i, row 16 rb + n
-  float m, l;      // running reference max (log2 units) and this lane's part of the sum
+  float m;         // running reference max (log2 units)
+  f32x4 lsum;      // P . ones: every element holds the row sum of the rounded probabilities
 };
 
 // Per-lane LDS byte offsets inside a tile slot, fixed for the kernel.
@@ -346,17 +347,16 @@ __device__ __forceinline__ void finish_tile(const Params& p, const Piece& P, con
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[tb][i] = __builtin_amdgcn_exp2f(x[tb][i] - m_ref);
   // P^T operand: MFMA K index 8 g + c <-> token 4 g + c (c < 4) or
-  // 16 + 4 g + c - 4; the sum takes the rounded probabilities, so the output
-  // is an exact weighted mean of the V rows
+  // 16 + 4 g + c - 4.  The row sum takes the rounded probabilities, so the
+  // output is an exact weighted mean of the V rows; it comes from one more
+  // MFMA against a tile of ones (all 32 tokens, no cross-lane reduction)
   const uint4 pw = make_uint4(pack2<QT>(pr[0][0], pr[0][1]), pack2<QT>(pr[0][2], pr[0][3]),
                               pack2<QT>(pr[1][0], pr[1][1]), pack2<QT>(pr[1][2], pr[1][3]));
-  const float2 r0 = unpack2<QT>(pw.x), r1 = unpack2<QT>(pw.y);
-  const float2 r2 = unpack2<QT>(pw.z), r3 = unpack2<QT>(pw.w);
-  A.l = A.l * alpha + (((r0.x + r0.y) + (r1.x + r1.y)) + ((r2.x + r2.y) + (r3.x + r3.y)));
   A.m = m_new;
   if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
     for (int m = 0; m < 16; ++m) A.o[m] *= alpha;
+    A.lsum *= alpha;
   }
   // ---- 3. O^T += V^T . P^T over dims [256 h, 256 h + 256), 16 (MFMA m) at
   // a time.  The V^T operand comes from two transposed reads, one per half
@@ -376,6 +376,8 @@ __device__ __forceinline__ void finish_tile(const Params& p, const Piece& P, con
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, kVAhead, 0);
+  const uint32_t one2 = QT == kBF16 ? 0x3f803f80u : 0x3c003c00u;
+  A.lsum = mfma_k32<QT>(make_uint4(one2, one2, one2, one2), pw, A.lsum);
 }
 
 // A run: tiles [begin, end) whose pages (at most 64, from pg_begin) have
@@ -452,7 +454,7 @@ __device__ __forceinline__ void stream_piece(const Params& p, const Piece& P, co
 
 __device__ __forceinline__ void reset(Acc& A) {
   A.m = kNegInf;
-  A.l = 0.f;
+  A.lsum = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int m = 0; m < 16; ++m) A.o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
@@ -464,7 +466,7 @@ __device__ __forceinline__ void finish_piece(const Params& p, const Piece& P, Ac
                                              int64_t prow0) {
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4, w = wave_id();
   const int row = 16 * (w & 3) + n, h = w >> 2;
-  const float l = sum_across_rows(A.l);
+  const float l = A.lsum[0];
   if (row >= p.R) return;
   // lane (n, g) holds dims 256 h + 16 m + 4 g + i of its row
   if (complete) {
