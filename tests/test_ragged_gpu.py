@@ -155,3 +155,35 @@ def test_ragged_bad_arguments_are_rejected():
     with pytest.raises(pkv.PkvError):     # non-finite scale
         pkv.ragged_attn(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_q"], inp["cu_seqlens_k"],
                         max_q_len=4, sm_scale=math.inf)
+
+
+def test_ragged_graph_capture_replays_match_eager():
+    # the call allocates nothing and issues one kernel, so it can be captured;
+    # each replay, with eager work in between, gives the eager result
+    inp = synth.make_ragged([70, 33], [90, 33], 4, 2, 128, 128, torch.bfloat16, 9, DEV)
+    out = torch.empty((103, 4, 128), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((4, 103), dtype=torch.float32, device=DEV)
+
+    def call():
+        pkv.ragged_attn(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_q"], inp["cu_seqlens_k"],
+                        max_q_len=70, sm_scale=0.1, causal=True, out=out, lse=lse)
+
+    call()
+    torch.cuda.synchronize()
+    want, want_lse = out.clone(), lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()                                   # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for _ in range(3):
+        out.fill_(0)
+        lse.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want) and torch.equal(lse, want_lse)
