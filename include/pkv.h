@@ -346,7 +346,9 @@ pkv_status pkv_merge_attn_states(void* out, const void* prefix_out, int64_t pref
  *   lse(row, h)  = log sum_j e^(sm_scale q.k_j)  (natural log, fp32, element
  *                  (row, h) at lse + row * lse_stride_n + h * lse_stride_h,
  *                  e.g. [H, N]: strides 1, total_q; lse may be NULL)
- * sm_scale must be positive and finite.
+ * sm_scale must be positive and finite.  K and V rows of a sequence must be
+ * finite (a causal query's weight for a later key is zero, but a zero times
+ * a non-finite value is not); rows outside every sequence are never used.
  * A query that sees no key gets zeros and lse = -inf.  dtype PKV_BF16 or
  * PKV_F16 for q, k, v and out; fp32 accumulation.  (head_dim_qk,
  * head_dim_v) in {(64, 64), (128, 128), (192, 128)}; total_k * num_kv_heads *

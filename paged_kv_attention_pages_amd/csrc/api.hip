@@ -660,8 +660,9 @@ pkv_status pkv_ragged_attn(const void* q, const void* k, const void* v, const in
     return fail(PKV_ERR_INVALID_ARGUMENT, "log-sum-exp strides must be non-negative");
   if (num_seqs > 65535 || Hq > 65535)
     return fail(PKV_ERR_UNSUPPORTED, "ragged_attn: at most 65535 sequences and query heads");
-  if ((int64_t)total_k * Hkv * (Dqk > Dv ? Dqk : Dv) * 2 >= ((int64_t)1 << 31) ||
-      (int64_t)total_q * Hq * Dqk >= ((int64_t)1 << 40))
+  // the kernel addresses K and V through buffer resources with 32-bit offsets
+  // (q, out and lse use 64-bit offsets)
+  if ((int64_t)total_k * Hkv * (Dqk > Dv ? Dqk : Dv) * 2 >= ((int64_t)1 << 31))
     return fail(PKV_ERR_UNSUPPORTED, "ragged_attn: K/V tensors must be under 2 GiB");
   if (num_seqs == 0 || max_q_len == 0 || total_q == 0) {
     g_err.clear();
