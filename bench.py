@@ -435,6 +435,9 @@ def bench_ragged(args):
     achieved = flops / (kern_ms * 1e-3) / 1e12
     print(f"[bench] {args.workload}: {ms * 1e3:.1f} us/call wall, evented {kern_ms * 1e3:.1f} us, "
           f"{value:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    cpu = None
+    if not getattr(args, "no_cpu_baseline", True):
+        cpu = ragged_cpu_baseline(cfg, inp, args.cpu_seconds)
     rec = {
         "metric": "ragged attention TFLOP/s (visible query-key pairs) + us/call",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K_, "warmup": W_,
@@ -449,9 +452,42 @@ def bench_ragged(args):
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "algorithmic_flops": flops,
                      "launch_us_mean": round(kern_ms * 1e3, 2)},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def ragged_cpu_baseline(cfg, inp, budget_s):
+    """The fp64 oracle on a bounded sample of the ragged workload: the last
+    queries of the first sequence (the ones that see the most keys), one head
+    at a time, as many heads as fit in the budget; TFLOP/s of the same
+    algorithmic flop count."""
+    import oracle
+    Lq, Lk = cfg["lens_q"][0], cfg["lens_k"][0]
+    nq = min(Lq, 64)
+    q = inp["q"][Lq - nq:Lq].cpu()
+    k = inp["k"][:Lk].cpu()
+    v = inp["v"][:Lk].cpu()
+    G = cfg["H"] // cfg["Hkv"]
+    flops = 0
+    t0 = time.perf_counter()
+    heads = 0
+    for h in range(cfg["H"]):
+        kv = h // G
+        # queries Lq - nq .. Lq - 1 of the sequence (aligned to the end of
+        # its Lk keys, as in the full call) over their keys
+        oracle.ragged_attn(q[:, h:h + 1], k[:, kv:kv + 1], v[:, kv:kv + 1], [0, nq], [0, Lk],
+                           sm_scale=cfg["Dqk"] ** -0.5, causal=cfg["causal"])
+        heads += 1
+        for i in range(Lq - nq, Lq):
+            vis = min(Lk, max(0, i + Lk - Lq + 1)) if cfg["causal"] else Lk
+            flops += 2 * vis * (cfg["Dqk"] + cfg["Dv"])
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": torch.get_num_threads(),
+            "kind": "oracle",
+            "sample": f"last {nq} queries of sequence 0 over its {Lk} keys, {heads} of {cfg['H']} heads, fp64"}
 
 
 def bench_insert(args):
