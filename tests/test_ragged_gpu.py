@@ -187,3 +187,51 @@ def test_ragged_graph_capture_replays_match_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, want) and torch.equal(lse, want_lse)
+
+
+# the two ragged bench workloads, at their full sizes: qk 192 / v 128, 64 heads,
+# 4 x 4096 new tokens (causal) and 2 x 1024 queries over 16384 keys
+FULL = {
+    "ragged_prefill": dict(lens_q=[4096] * 4, lens_k=[4096] * 4, causal=True),
+    "ragged_context": dict(lens_q=[1024] * 2, lens_k=[16384] * 2, causal=False),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_ragged_full_size_sampled(name):
+    # one launch at the full size; sampled (sequence, query, head) outputs and
+    # log-sum-exps against the oracle, each computed alone: query i of a
+    # causal sequence attends exactly its first i + 1 + Lk - Lq keys
+    cfg = FULL[name]
+    H, Dqk, Dv = 64, 192, 128
+    print(f"[case] ragged full {name}", flush=True)
+    inp = synth.make_ragged(cfg["lens_q"], cfg["lens_k"], H, H, Dqk, Dv, torch.bfloat16, 1, DEV)
+    scale = Dqk ** -0.5
+    out, lse = pkv.ragged_attn(inp["q"], inp["k"], inp["v"], inp["cu_seqlens_q"],
+                               inp["cu_seqlens_k"], max_q_len=inp["max_q_len"], sm_scale=scale,
+                               causal=cfg["causal"], return_lse=True)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any()
+    cq, ck = inp["cu_seqlens_q_host"], inp["cu_seqlens_k_host"]
+    g = torch.Generator().manual_seed(2)
+    worst = 0.0
+    for s in range(len(cfg["lens_q"])):
+        Lq, Lk = cfg["lens_q"][s], cfg["lens_k"][s]
+        queries = sorted({0, Lq - 1, *torch.randint(0, Lq, (4,), generator=g).tolist()})
+        for i in queries:
+            h = int(torch.randint(0, H, (1,), generator=g))
+            n = min(Lk, i + 1 + Lk - Lq) if cfg["causal"] else Lk
+            row = cq[s] + i
+            q1 = inp["q"][row:row + 1, h:h + 1].cpu()
+            k1 = inp["k"][ck[s]:ck[s] + n, h:h + 1].cpu()
+            v1 = inp["v"][ck[s]:ck[s] + n, h:h + 1].cpu()
+            ref, ref_lse = oracle.ragged_attn(q1, k1, v1, [0, 1], [0, n], sm_scale=scale,
+                                              causal=False)
+            got = out[row, h].double().cpu()
+            d = (got - ref[0, 0]).abs()
+            allowed = torch.clamp(_half_ulp(ref[0, 0], torch.bfloat16) + 0.5 * TOL[torch.bfloat16],
+                                  min=TOL[torch.bfloat16])
+            assert not (d > allowed).any(), f"{name} seq {s} query {i} head {h}: {d.max().item()}"
+            assert abs(float(lse[h, row]) - float(ref_lse[0, 0])) <= LSE_TOL[torch.bfloat16]
+            worst = max(worst, d.max().item())
+    print(f"[parity] ragged full {name}: max_abs={worst:.3e}", flush=True)
