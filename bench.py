@@ -450,7 +450,7 @@ def bench_ragged(args):
         "roofline": {"kernel": "ragged attention (mfma)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "algorithmic_flops": flops,
+                     "traffic": measured_traffic(args.workload, False), "algorithmic_flops": flops,
                      "launch_us_mean": round(kern_ms * 1e3, 2)},
         "cpu_baseline": cpu,
     }
