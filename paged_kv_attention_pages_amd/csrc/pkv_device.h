@@ -269,20 +269,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // decode: split kernel 193.7 us with the default policy, 173.8 us with nt.
 constexpr int kStreamPolicy = 2;
 
-// N 32-bit words at byte offset voff + soff (K/V stream: non-temporal)
-template <int N>
+// N 32-bit words at byte offset voff + soff (K/V stream: non-temporal unless
+// the caller asks for another policy)
+template <int N, int POL = kStreamPolicy>
 __device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint32_t* w) {
   if constexpr (N >= 4) {
 #pragma unroll
     for (int i = 0; i < N; i += 4) {
-      u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 4 * i, soff, kStreamPolicy);
+      u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 4 * i, soff, POL);
       w[i] = a[0]; w[i + 1] = a[1]; w[i + 2] = a[2]; w[i + 3] = a[3];
     }
   } else if constexpr (N == 2) {
-    u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStreamPolicy);
+    u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, POL);
     w[0] = a[0]; w[1] = a[1];
   } else {
-    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStreamPolicy);
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, POL);
   }
 }
 
