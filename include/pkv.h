@@ -358,7 +358,8 @@ pkv_status pkv_merge_attn_states(void* out, const void* prefix_out, int64_t pref
  * stay in bounds.  Queries past `max_q_len` in a sequence are not computed
  * (their rows are left unwritten): max_q_len must be at least the longest
  * Lq (the page's `max_q_len`).  Pointers 16-byte aligned (lse 4-byte).
- * Caller-owned memory, nothing allocated; one launch on `stream`. */
+ * Caller-owned memory, nothing allocated; one launch on `stream`.  (ABI
+ * version 6.) */
 pkv_status pkv_ragged_attn(const void* q, const void* k, const void* v,
                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* out,
                            float* lse, int64_t lse_stride_n, int64_t lse_stride_h, int num_seqs,
