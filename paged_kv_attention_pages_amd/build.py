@@ -18,7 +18,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "split_mfma.hip", "split_mla.hip", "split_valu.hip", "combine.hip",
+SOURCES = ["api.hip", "split_mfma.hip", "split_mla.hip", "split_mla_ws.hip", "split_valu.hip", "combine.hip",
            "cache_insert.hip", "head_matmul.hip", "merge_states.hip", "ragged_attn.hip"]
 LIB = os.path.join(HERE, "libpkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")

@@ -65,6 +65,7 @@ struct Plan {
   size_t ws_ml_off;    // offset of (max, sum) pairs
   size_t ws_cnt_off;   // offset of the per-unit counters (single-launch merge)
   bool fused;          // cut units merged in the split kernel (no combine launch)
+  bool lat_ws;         // latent stream-K with separate score / P.V waves (16-bit cache)
   size_t ws_bytes;
 };
 
@@ -186,6 +187,7 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
   pl->sk_waves = 0;
   pl->sk_hb = 1;
   pl->fused = false;
+  pl->lat_ws = false;
   pl->ws_cnt_off = 0;
   // Stream-K schedule (matrix-core path, batch <= 256, no forced split size):
   // persistent waves (measured best: one per SIMD for 16-bit caches, each
@@ -216,7 +218,10 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
         }
     pl->split_pages = 0;
     pl->max_splits = 0;
-    const size_t nrow = (size_t)2 * pl->sk_waves * R;
+    // the latent kernel for 16-bit caches keeps 64 padded rows per slot, its
+    // partial outputs in the P.V waves' register order (see combine.hip)
+    pl->lat_ws = path == PKV_PATH_MFMA_MLA && d->kv_dtype != PKV_FP8_E4M3;
+    const size_t nrow = (size_t)2 * pl->sk_waves * (pl->lat_ws ? 64 : R);
     pl->ws_o_bytes = nrow * Dv * sizeof(float);
     pl->ws_ml_off = (pl->ws_o_bytes + 255) & ~(size_t)255;
     pl->ws_bytes = pl->ws_ml_off + nrow * 2 * sizeof(float);
@@ -335,6 +340,7 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
   p.kv_scale = kv_scale;
   p.qk_unit = (float)(1.4426950408889634 / std::sqrt((double)Dk));
   p.fused = pl.fused ? 1 : 0;
+  p.ws_lanes = pl.lat_ws ? 1 : 0;
   p.out_fp8 = out_fp8 ? 1 : 0;
   p.rcp_out_scale = rcp_out;
   p.ws_cnt = pl.fused ? (unsigned long long*)((char*)workspace + pl.ws_cnt_off) : nullptr;
@@ -346,7 +352,12 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
   hipError_t e;
   switch (pl.path) {
     case PKV_PATH_VALU: e = pkv::launch_split_valu(d->q_dtype, d->kv_dtype, (int)Dk, p, s); break;
-    case PKV_PATH_MFMA_MLA: e = pkv::launch_split_mla(d->q_dtype, d->kv_dtype, p, s); break;
+    case PKV_PATH_MFMA_MLA:
+      // 16-bit caches on the stream-K schedule: the wave-specialised kernel;
+      // fp8 caches and the split grid: the kernel that stages tiles in registers
+      e = pl.lat_ws ? pkv::launch_split_mla_ws(d->q_dtype, p, s)
+              : pkv::launch_split_mla(d->q_dtype, d->kv_dtype, p, s);
+      break;
     default: e = pkv::launch_split_mfma16(d->q_dtype, d->kv_dtype, (int)Dk, p, s); break;
   }
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "split-KV launch failed: %s", hipGetErrorString(e));

@@ -139,8 +139,102 @@ __global__ __launch_bounds__(64) void combine_sk_kernel(Params p) {
   store_out4<QT>(p, ob + 4, acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
 }
 
+// Stream-K merge of the latent kernel's partials (split_mla_ws.hip), which
+// sit in the P.V waves' register order: slot s holds, for P.V wave pw (rows
+// 32 (pw / 2) .., dims 256 (pw % 2) ..), element (j, 4 q + e) of lane l at
+// float ((s * 4 + pw) * 32 + 4 j + q) * 256 + 4 l + e, where lane l holds row
+// 32 (pw / 2) + l % 32 and dims 256 (pw % 2) + 32 j + 8 q + 4 (l / 32) + e;
+// (m, l) of row r at ws_ml[64 s + r].  One wave per (unit, P.V block, j):
+// each lane merges 16 values of its row over the unit's slots, in chunks of 8
+// slots loaded together (one memory round trip per chunk), and every load
+// instruction reads 1 KB contiguously.
+template <int QT>
+__global__ __launch_bounds__(64) void combine_lat_kernel(Params p) {
+  constexpr int CH = 8;
+  resolve_scales(p);
+  const int pw = blockIdx.x >> 3, j = blockIdx.x & 7, kvh = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  const int r = 32 * (pw >> 1) + (lane & 31);
+  const bool row_ok = r < p.R;
+  const int rr = row_ok ? r : 0;  // lanes past the last row read row 0 and store nothing
+  const SkSched S = sk_schedule(p);
+  const int W = sk_waves_eff(S.T, p.sk_waves);
+  int pre, n;
+  sk_seq_of(S, b, &pre, &n);
+  const int64_t ob = q_row_offset(p, b, kvh, rr) * p.Dv + 256 * (pw & 1) + 32 * j + 4 * h;
+  if (n == 0) {
+    if (row_ok)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) store_out4<QT>(p, ob + 8 * q, 0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const int64_t us = sk_unit_start(S, kvh, pre), ue = us + n;
+  const int w0 = sk_wave_of(S.T, us, W), w1 = sk_wave_of(S.T, ue - 1, W);
+  if (w0 == w1) return;
+  const int64_t slot0 = sk_wave_start(S.T, w0, W) == us ? 2 * (int64_t)w0 : 2 * (int64_t)w0 + 1;
+  const int nslots = w1 - w0 + 1;
+  float M = kNegInf, den = 0.f;
+  if (p.sinks != nullptr) {
+    M = p.sinks[kvh * p.G + rr % p.G] * kLog2e;
+    den = 1.f;
+  }
+  float acc[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) acc[k] = 0.f;
+  for (int j0 = 0; j0 < nslots; j0 += CH) {
+    float2 ml[CH];
+    float4 v[CH][4];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int js = j0 + u;
+      const int64_t slot = js >= nslots || js == 0 ? slot0 : 2 * (int64_t)(w0 + js);
+      ml[u] = p.ws_ml[slot * 64 + rr];
+      const float4* src = (const float4*)(p.ws_o + ((slot * 4 + pw) * 32 + 4 * j) * 256) + lane;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[u][q] = src[64 * q];
+    }
+    float Mc = M;
+#pragma unroll
+    for (int u = 0; u < CH; ++u)
+      if (j0 + u < nslots) Mc = fmaxf(Mc, ml[u].x);
+    if (Mc == kNegInf) continue;
+    const float scale = exp2f(M - Mc);
+    den *= scale;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] *= scale;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const float wu = (j0 + u < nslots && ml[u].x != kNegInf) ? exp2f(ml[u].x - Mc) : 0.f;
+      den += wu * ml[u].y;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[4 * q] += wu * v[u][q].x;
+        acc[4 * q + 1] += wu * v[u][q].y;
+        acc[4 * q + 2] += wu * v[u][q].z;
+        acc[4 * q + 3] += wu * v[u][q].w;
+      }
+    }
+    M = Mc;
+  }
+  if (!row_ok) return;
+  const float inv = den > 0.f ? p.out_scale / den : 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    store_out4<QT>(p, ob + 8 * q, acc[4 * q] * inv, acc[4 * q + 1] * inv, acc[4 * q + 2] * inv,
+                   acc[4 * q + 3] * inv);
+}
+
 hipError_t launch_combine(int q_dtype, const Params& p, hipStream_t s) {
   dim3 grid(p.R, p.Hkv, p.B);
+  if (p.ws_lanes) {
+    if (p.Dv != 512 || p.R > 64) return hipErrorInvalidValue;
+    const dim3 lgrid(32, p.Hkv, p.B);
+    if (q_dtype == kBF16)
+      hipLaunchKernelGGL((combine_lat_kernel<kBF16>), lgrid, dim3(64), 0, s, p);
+    else
+      hipLaunchKernelGGL((combine_lat_kernel<kF16>), lgrid, dim3(64), 0, s, p);
+    return hipGetLastError();
+  }
   if (p.sk_waves > 0) {
 #define PKV_COMBINE_SK(DV)                                                                   \
   if (p.Dv == DV) {                                                                          \

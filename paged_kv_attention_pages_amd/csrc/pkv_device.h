@@ -51,6 +51,9 @@ struct Params {
   // round(out * rcp_out_scale); 0 = 16-bit output in q's dtype
   int out_fp8;
   float rcp_out_scale;
+  // latent stream-K partials in the P.V waves' register order, 64 rows a
+  // slot (split_mla_ws.hip; merged by combine_lat_kernel)
+  int ws_lanes;
 };
 
 // Scales from device memory when the call passed them there: every kernel
