@@ -20,6 +20,13 @@ Reported (one JSON line on stdout):
                bytes per launch / its mean time, against the HBM peak
   cpu_baseline the fp64 oracle on a bounded sample of the same batch, on the
                host cores (a reported baseline, not the target)
+  configs      (default run) the other decode configurations measured the same
+               way in the same run -- tiny, fp8 + window + sinks, speculative
+               decode, latent (MLA) and its fp8 form: us/call, effective GB/s,
+               % of HBM peak, the split-KV kernel's fraction of peak (and, for
+               the latent kernel, of the bf16 matrix-core peak), the combine
+               time and an oracle baseline on a smaller sample
+Each workload's seed is its number in the list of configurations.
 Algorithmic KV bytes = sum over sequences of (tokens some query row can see)
 x num_kv_heads x (head_dim_qk + head_dim_v) x element size; a latent cache
 row serves as K and V and counts once.
@@ -107,6 +114,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure only the named workload (the default run also measures the other "
+                         "decode configurations and reports them under 'configs')")
+    ap.add_argument("--config-cpu-seconds", type=float, default=5.0,
+                    help="approximate CPU time budget of each other configuration's oracle baseline")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -130,10 +142,39 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = synth.WORKLOADS[args.workload]
-    L = synth.draw_seq_lens(w, 1)
+    rec = measure_decode(args.workload, args, args.cpu_seconds, headline=True)
+    if args.workload == "llama3_8b_gqa" and not args.no_configs and not (args.path or args.split_pages or
+                                                                          args.target_ctas):
+        # every other decode configuration, measured in the same run
+        cfgs = {}
+        for name in ["tiny", "fp8_window_sinks", "spec_decode", "mla", "mla_fp8"]:
+            torch.cuda.empty_cache()
+            cfgs[name] = measure_decode(name, args, args.config_cpu_seconds, headline=False)
+        rec["configs"] = cfgs
+    print(json.dumps(rec), flush=True)
+
+
+# The seed of each decode workload: its number in the list of synthetic
+# configurations (the fp8 latent form shares the latent workload's draw).
+SEEDS = {"tiny": 1, "llama3_8b_gqa": 2, "fp8_window_sinks": 3, "spec_decode": 4, "mla": 5,
+         "mla_fp8": 5}
+
+
+def measure_decode(name, args, cpu_budget, headline):
+    """One decode workload: wall time over K back-to-back calls, then an
+    evented pass that splits each call into the split-KV kernel and the
+    combine; the oracle on a bounded sample of the same batch.  Returns the
+    JSON record (the top-level line for the headline workload, a compact
+    sub-record otherwise)."""
+    import paged_kv_attention_pages_amd as pkv
+    from paged_kv_attention_pages_amd import synth
+
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[name]
+    seed = SEEDS.get(name, 1)
+    L = synth.draw_seq_lens(w, seed)
     kf = (L - w.q_seq_len + 1 - w.window).clamp(min=0) if w.window > 0 else None
-    inp = synth.make_inputs(w, seed=1, device=dev, seq_lens=L, keep_from=kf)
+    inp = synth.make_inputs(w, seed=seed, device=dev, seq_lens=L, keep_from=kf)
     cache_bytes = inp["k_cache"].numel() * inp["k_cache"].element_size()
     if not w.v_from_k:
         cache_bytes += inp["v_cache"].numel() * inp["v_cache"].element_size()
@@ -203,12 +244,43 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, inp, L, args.cpu_seconds)
-
+        cpu = cpu_baseline(w, inp, L, cpu_budget)
+    traffic = measured_traffic(w.name, bool(args.path or args.split_pages or args.target_ctas))
+    path = pkv.PATH_NAMES.get(plan["path"], plan["path"])
+    del reps, inp
     dtype = {torch.bfloat16: "bf16", torch.float16: "f16", torch.float8_e4m3fn: "fp8"}[w.q_dtype]
     if w.kv_dtype == torch.float8_e4m3fn:
         dtype += "+fp8kv"
-    rec = {
+    cfg = {
+        "workload": w.name, "seed": seed, "batch": B, "q_seq_len": w.q_seq_len,
+        "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+        "head_dim_qk": w.head_dim_qk, "head_dim_v": w.head_dim_v,
+        "kv_layout": w.kv_layout, "page_size": w.page_size,
+        "seq_len_range": list(w.seq_len_range) if w.seq_len_range else list(w.fixed_seq_lens),
+        "window": w.window, "sinks": w.sinks, "mask": w.mask,
+        "kv_dtype": str(w.kv_dtype).replace("torch.", ""),
+        "kv_bytes_per_call": kv_bytes, "cache_replicas": n_rep, "path": path,
+        "split_pages": plan["split_pages"], "max_splits": plan["max_splits"],
+        "single_launch": bool(plan["single_launch"]),
+    }
+    if not headline:
+        sub = {
+            "config": cfg, "dtype": dtype, "us_per_call": round(ms_per_step * 1e3, 2),
+            "us_per_call_evented_median": round(statistics.median(call_ms) * 1e3, 2),
+            "us_per_call_evented_p10_p90": [round(q * 1e3, 2) for q in _p10_p90(call_ms)],
+            "effective_gbs": round(value, 2), "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+            "split_us_mean": round(split_mean * 1e3, 2),
+            "split_frac_hbm_peak": round(achieved / HBM_PEAK_GBS, 4),
+            "combine_us_mean": round(statistics.fmean(comb_ms) * 1e3, 2),
+            "traffic": traffic, "cpu_baseline": cpu,
+        }
+        if path == "mfma_mla":
+            # matrix-core work: every visible token x rows x (Dqk + Dv) x 2 flop
+            vis = int((L - ((L - w.q_seq_len + 1 - w.window).clamp(min=0) if w.window > 0 else 0)).sum())
+            flops = 2.0 * vis * w.num_q_heads * w.q_seq_len * (w.head_dim_qk + w.head_dim_v)
+            sub["split_mfma_frac"] = round(flops / (split_mean * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        return sub
+    return {
         "metric": "effective KV GB/s (% of HBM peak) + us/call, paged GQA decode attention",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
@@ -217,29 +289,15 @@ def main():
         "us_per_call_evented_median": round(statistics.median(call_ms) * 1e3, 2),
         "us_per_call_evented_p10_p90": [round(q * 1e3, 2) for q in _p10_p90(call_ms)],
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "config": {
-            "workload": w.name, "batch": B, "q_seq_len": w.q_seq_len,
-            "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
-            "head_dim_qk": w.head_dim_qk, "head_dim_v": w.head_dim_v,
-            "kv_layout": w.kv_layout, "page_size": w.page_size,
-            "seq_len_range": list(w.seq_len_range) if w.seq_len_range else list(w.fixed_seq_lens),
-            "window": w.window, "kv_dtype": str(w.kv_dtype).replace("torch.", ""),
-            "kv_bytes_per_call": kv_bytes, "cache_replicas": n_rep,
-            "path": pkv.PATH_NAMES.get(plan["path"], plan["path"]),
-            "split_pages": plan["split_pages"], "max_splits": plan["max_splits"],
-            "single_launch": bool(plan["single_launch"]),
-        },
+        "config": cfg,
         "roofline": {
-            "kernel": "split-KV decode (" + pkv.PATH_NAMES.get(plan["path"], "?") + ")",
+            "kernel": "split-KV decode (" + path + ")",
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name, bool(args.path or args.split_pages or args.target_ctas)),
-            "algorithmic_bytes": kv_bytes,
-            "launch_us_mean": round(split_mean * 1e3, 2),
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes": kv_bytes, "launch_us_mean": round(split_mean * 1e3, 2),
         },
         "cpu_baseline": cpu,
     }
-    print(json.dumps(rec), flush=True)
 
 
 # The write side (cache insert).  Shapes: the prefill inserts write one
