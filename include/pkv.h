@@ -38,8 +38,10 @@
  *   (the draft tokens are the last q_seq_len positions of the sequence).
  *   Token t is visible to (b, i, h) iff
  *       t < seq_len,
- *       window == 0  or  t > pos - window          (the last `window` tokens,
- *                                                   the query's own included),
+ *       window == 0  or  t > pos - window          (a lower bound only: the
+ *                                                   window hides no token after
+ *                                                   pos; those are hidden only
+ *                                                   by the mask),
  *       q_seq_len == 1 or mask == NULL or t < seq_len - q_seq_len
  *                  or bit (t - (seq_len - q_seq_len)) of mask row (b, i) is 1.
  *   A mask row is read as little-endian 32-bit words, word w being

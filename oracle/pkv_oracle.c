@@ -31,7 +31,10 @@
  *   - a sink is a logit-domain value: it adds e^(sink - M) to the softmax
  *     denominator and nothing to the numerator, once per (sequence, query
  *     token, head); head h uses sinks[h / G][h % G].
- *   - window W > 0: position pos sees t iff pos - W < t <= pos.
+ *   - window W > 0 bounds visibility from below only: position pos sees t
+ *     only if t > pos - W.  No upper bound comes from the window; tokens
+ *     after pos are hidden only by the draft mask (and t < seq_len), so a
+ *     NULL mask with q_seq_len > 1 lets every draft see every other draft.
  *   - the q_seq_len draft tokens are the last positions of the sequence; a
  *     mask row is little-endian 32-bit words made of uint16 pairs, bit j set
  *     means draft j is visible; tokens before the drafts are always visible;

@@ -432,7 +432,7 @@ __device__ __forceinline__ int64_t q_row_offset(const Params& p, int b, int kvh,
 // score fragment (the bit test was dropped), so every term is evaluated and
 // combined with bitwise operators.
 struct RowVis {
-  int lo;          // first visible token (window), may be negative
+  int lo;          // first visible token (the window is a lower bound only), may be negative
   int draft0;      // first draft position L - Tq (mask applies from here)
   uint32_t bits;   // draft mask bits of this row (all ones without a mask)
   __device__ __forceinline__ bool operator()(int t, int L) const {

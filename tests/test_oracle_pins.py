@@ -188,6 +188,25 @@ def test_spec_mask_matches_dense(kind, W):
     torch.testing.assert_close(got, want, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("kind", [None, "ones"])
+def test_window_is_a_lower_bound_only_with_a_non_causal_mask(kind):
+    # The window hides tokens before pos - W + 1 and nothing after pos: with a
+    # NULL or all-ones mask a draft still sees the drafts that follow it.
+    W = 5
+    w = small("spec", mask=kind, window=W, seq_len_range=(6, 60))
+    inp = synth.make_inputs(w, seed=21)
+    got = run_oracle(w, inp)
+    want = dense.dense_decode(inp, num_kv_heads=w.num_kv_heads, page_size=w.page_size,
+                              kv_layout=w.kv_layout, visible_fn=window_visible(W, w.q_seq_len))
+    torch.testing.assert_close(got, want, rtol=0, atol=1e-12)
+    # the reading that also cuts at t <= pos gives a different result here
+    causal = dense.dense_decode(
+        inp, num_kv_heads=w.num_kv_heads, page_size=w.page_size, kv_layout=w.kv_layout,
+        visible_fn=lambda b, i, L: window_visible(W, w.q_seq_len)(b, i, L)
+        & (torch.arange(L) <= L - w.q_seq_len + i))
+    assert (got[:, :-1] - causal[:, :-1]).abs().max() > 1e-3
+
+
 def test_mask_with_33_drafts_uses_second_word():
     # q_seq_len 33: each row has two 32-bit words; draft 32 lives in word 1
     w = small("spec", q_seq_len=33, num_q_heads=8, num_kv_heads=8, mask="random",

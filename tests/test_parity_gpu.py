@@ -168,7 +168,7 @@ def test_fp16_query_fp8_cache():
         assert_parity(w, got, run_oracle(w, inp), f"f16q-fp8/{path}")
 
 
-@pytest.mark.parametrize("kind", ["causal", "random", "ones"])
+@pytest.mark.parametrize("kind", ["causal", "random", "ones", None])
 @pytest.mark.parametrize("W", [0, 50])
 def test_spec_decode_masks(kind, W):
     w = SMALL["spec"].replace(mask=kind, window=W)
