@@ -205,8 +205,10 @@ size_t pkv_workspace_size(const pkv_dims* dims, int num_kv_heads, int page_size,
  * `semaphores` live in the workspace: on the matrix-core stream-K plan the
  * last wave to finish a piece of a (sequence, KV head) merges its partials
  * in the same launch; the latent-cache and split-grid plans merge in a second
- * kernel.  `sm_count`, `enable_pdl` and `rcp_out_scale` have no counterpart:
- * the CU count is queried and the output scale is 1. */
+ * kernel.  `sm_count` and `enable_pdl` have no counterpart (the CU count is
+ * queried).  This entry point writes the output in q's dtype with scale 1;
+ * the xqa page's `rcp_out_scale` and fp8 output are pkv_options.out_fp8 and
+ * pkv_options.rcp_out_scale of pkv_decode_attn_ex. */
 pkv_status pkv_decode_attn(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* page_table, const uint32_t* seq_lens,
                            void* out, void* workspace, int num_kv_heads,

@@ -10,8 +10,9 @@ library raises.
 (reference page: q, k_cache, v_cache, page_table, seq_lens, output,
 workspace_buffer, num_kv_heads, page_size, sinks, q_scale, kv_scale,
 sliding_win_size, kv_layout, q_seq_len, mask).  The workspace, when not
-given, is cached per device and grown on demand, as the vllm-omni trtllm_attn
-backend page does with its attention workspace (``_get_workspace``).
+given, is cached per (device, stream) and grown on demand, as the vllm-omni
+trtllm_attn backend page does with its attention workspace (``_get_workspace``);
+calls on different streams never share one.
 """
 from __future__ import annotations
 
@@ -212,11 +213,22 @@ def workspace_size(*, batch, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v,
 _ws_cache: dict = {}
 
 
-def _workspace(device, nbytes: int) -> torch.Tensor:
-    ws = _ws_cache.get(device)
+def _workspace(device, stream: int, nbytes: int) -> torch.Tensor:
+    """The default workspace of (device, stream), grown on demand.
+
+    Calls on one stream run in order and may share it; calls on another
+    stream get their own, since two calls in flight at once would write the
+    same partial slots and counters.  A workspace used on a stream other than
+    torch's current one is marked with record_stream, so that dropping it
+    when it grows cannot hand its memory out while a kernel still uses it.
+    """
+    key = (device, stream)
+    ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _ws_cache[device] = ws
+        if stream != torch.cuda.current_stream(device).cuda_stream:
+            ws.record_stream(torch.cuda.ExternalStream(stream, device=device))
+        _ws_cache[key] = ws
     return ws
 
 
@@ -311,7 +323,9 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
         _check(L.pkv_query_plan(ctypes.byref(d), num_kv_heads, page_size, sliding_win_size,
                                 q_seq_len, None if opts is None else ctypes.byref(opts),
                                 ctypes.byref(info)))
-        workspace_buffer = _workspace(q.device, info.workspace_bytes)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        workspace_buffer = _workspace(q.device, stream, info.workspace_bytes)
     d.workspace_bytes = workspace_buffer.numel() * workspace_buffer.element_size()
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream

@@ -194,10 +194,14 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
   // with a three-stage pipeline in flight); 2 partial slots per wave.
   // The latent-cache kernel runs the same schedule over 32-token tiles with
   // one four-wave workgroup per CU (its register budget allows no more).
-  // (its 32-bit tile counters need the whole tile stream under 2^31 tiles)
-  const bool sk_path =
-      path == PKV_PATH_MFMA ||
-      (path == PKV_PATH_MFMA_MLA && units * cdiv(pps * ps, 32) < ((int64_t)1 << 31));
+  // Both kernels count tiles in 32-bit integers (the tiles of one KV head
+  // over all sequences, per-sequence prefixes, unit offsets), so the whole
+  // tile stream must stay under 2^31 tiles; a sequence's visible tokens span
+  // at most cdiv(pages_max * ps, tile) + 1 aligned tiles.  Larger problems
+  // take the split grid.
+  const int64_t sk_tile = path == PKV_PATH_MFMA_MLA ? 32 : 16;
+  const bool sk_path = (path == PKV_PATH_MFMA || path == PKV_PATH_MFMA_MLA) &&
+                       units * (cdiv(pages_max * ps, sk_tile) + 1) < ((int64_t)1 << 31);
   if (sk_path && d->batch <= 256 && !(opts && opts->split_pages > 0)) {
     // fp8 tiles carry half the bytes for the same matrix work, so more waves
     // per CU hide the conversion work: 8 per CU for fp8, 4 for 16-bit caches

@@ -127,6 +127,21 @@ def test_plan_stream_k():
     assert plan(batch=300)["split_pages"] > 0
 
 
+def test_plan_stream_k_tile_count_edge():
+    # the stream-K kernels count tiles (16 tokens; 32 for the latent cache)
+    # in 32-bit integers: the last problem under 2^31 tiles keeps stream-K,
+    # the next page per sequence moves to the split grid
+    big = dict(batch=256, pages_per_seq=262143)          # 2048 units x (4 * pps + 1) tiles
+    assert plan(**big)["split_pages"] == 0
+    assert 2048 * (4 * 262143 + 1) < 2 ** 31
+    p = plan(**dict(big, pages_per_seq=262144))
+    assert p["split_pages"] > 0 and p["max_splits"] > 0
+    assert 2048 * (4 * 262144 + 1) >= 2 ** 31
+    lat = dict(batch=256, num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512)
+    assert plan(**lat, pages_per_seq=4194303)["split_pages"] == 0
+    assert plan(**lat, pages_per_seq=4194304)["split_pages"] > 0
+
+
 def test_plan_latent_fp8_cache_and_query():
     # the latent path takes an e4m3fn cache with a 16-bit or e4m3fn query
     lat = dict(head_dim_qk=576, head_dim_v=512, num_kv_heads=1, num_q_heads=64)

@@ -472,6 +472,33 @@ def test_repeated_calls_reuse_workspace():
         assert_parity(w, out, ref, "ws-reuse")
 
 
+def test_default_workspace_per_stream():
+    # two calls in flight on two streams with the default workspace: each
+    # stream has its own, so neither overwrites the other's partials
+    w = SMALL["gqa"].replace(batch=4, seq_len_range=(600, 1500))
+    print("[case] default workspace on two streams", flush=True)
+    a, b = make(w, seed=82), make(w, seed=83)
+    ref_a, ref_b = run_oracle(w, a), run_oracle(w, b)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for inp, s in ((a, s1), (b, s2)):
+        out = torch.full((w.batch, 1, w.num_q_heads, 128), float("nan"), dtype=w.q_dtype, device=DEV)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for inp, s, out in ((a, s1, outs[0]), (b, s2, outs[1])):
+            with torch.cuda.stream(s):
+                pkv.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"],
+                                inp["seq_lens"], out, num_kv_heads=w.num_kv_heads,
+                                page_size=w.page_size, kv_layout=w.kv_layout)
+    torch.cuda.synchronize()
+    keys = [k for k in pkv._ws_cache if k[1] in (s1.cuda_stream, s2.cuda_stream)]
+    assert len(keys) == 2
+    assert pkv._ws_cache[keys[0]].data_ptr() != pkv._ws_cache[keys[1]].data_ptr()
+    assert_parity(w, outs[0], ref_a, "ws-stream1")
+    assert_parity(w, outs[1], ref_b, "ws-stream2")
+
+
 # ---------------------------------------------------------------- single-launch merge
 
 def _ulps_apart(a, b, dtype):
