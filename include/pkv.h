@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 6
+#define PKV_ABI_VERSION 7
 
 typedef enum {
   PKV_OK = 0,
@@ -225,6 +225,29 @@ pkv_status pkv_decode_attn_ex(const void* q, const void* k_cache, const void* v_
                               float q_scale, float kv_scale, int window,
                               int q_seq_len, const uint16_t* mask, void* stream,
                               const pkv_dims* dims, const pkv_options* opts);
+
+/* Bytes of the static scratch of pkv_decode_attn_noalloc (per GPU). */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+
+/* pkv_decode_attn_ex without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The partial results and counters live in
+ * a static device array of PKV_NOALLOC_SCRATCH_BYTES bytes, one per GPU,
+ * allocated when the library's code is loaded on that GPU and kept until the
+ * process ends; this call allocates nothing.  The current device must be the
+ * one the stream and the buffers belong to.  A plan needing more scratch
+ * than that (pkv_query_plan's workspace_bytes) is rejected with
+ * PKV_ERR_WORKSPACE_TOO_SMALL before any device work.  Every call on one GPU
+ * shares its array: nothing in it needs clearing (the single-launch counters
+ * carry a per-call tag), but calls that overlap in time on one GPU (two
+ * streams, or two threads) race and give wrong results.  (ABI version 7.) */
+pkv_status pkv_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* page_table, const uint32_t* seq_lens,
+                                   void* out, int num_kv_heads, int page_size, int layout,
+                                   const float* sinks, float q_scale, float kv_scale,
+                                   int window, int q_seq_len, const uint16_t* mask,
+                                   void* stream, const pkv_dims* dims,
+                                   const pkv_options* opts);
 
 /* Checks the device-resident inputs the decode call trusts: every page id a
  * visible token needs lies in [0, num_pages) and q_seq_len <= seq_len <=

@@ -50,6 +50,10 @@ class Dims(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_uint64)]
 
 
+# bytes of the static per-GPU scratch of pkv_decode_attn_noalloc
+NOALLOC_SCRATCH_BYTES = 96 << 20
+
+
 class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("split_pages", ctypes.c_int32),
                 ("num_cus", ctypes.c_int32), ("target_ctas", ctypes.c_int32),
@@ -110,6 +114,8 @@ def lib():
                 L.pkv_decode_attn.argtypes = dec
                 L.pkv_decode_attn_ex.restype = ctypes.c_int
                 L.pkv_decode_attn_ex.argtypes = dec + [ctypes.POINTER(Options)]
+                L.pkv_decode_attn_noalloc.restype = ctypes.c_int
+                L.pkv_decode_attn_noalloc.argtypes = dec[:6] + dec[7:] + [ctypes.POINTER(Options)]
                 L.pkv_validate_inputs.restype = ctypes.c_int
                 L.pkv_validate_inputs.argtypes = [_vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                   ctypes.c_int, _vp, ctypes.POINTER(Dims)]
@@ -303,21 +309,11 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
     """
     if head_dim_v is None:
         head_dim_v = output.shape[-1]
-    if q.device.type != "cuda":
-        raise PkvError(1, "decode_attn runs on the GPU only: q must be a device tensor")
-    _shape_checks(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size,
-                  kv_layout, q_seq_len, head_dim_v, mask)
-    if sinks is not None:
-        if sinks.dtype != torch.float32 or sinks.numel() != q.shape[-2] or not sinks.is_contiguous():
-            raise PkvError(1, "sinks must be contiguous float32 [num_kv_heads, head_group_ratio]")
     L = lib()
-    ev = None if split_event is None else split_event.cuda_event
-    q_scale, q_scale_dev = _scale_arg(q_scale, "q_scale", q.device)
-    kv_scale, kv_scale_dev = _scale_arg(kv_scale, "kv_scale", q.device)
-    out_fp8 = output.dtype in (torch.float8_e4m3fn, torch.uint8)
-    opts = _options(path, split_pages, 0, target_ctas, ev, q_scale_dev, kv_scale_dev,
-                    single_launch, out_fp8, rcp_out_scale)
-    d = _dims(q, k_cache, page_table, head_dim_v, q_seq_len)
+    opts, d, q_scale, kv_scale = _decode_prep(
+        q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size, sinks,
+        q_scale, kv_scale, kv_layout, q_seq_len, mask, head_dim_v, path, split_pages,
+        target_ctas, split_event, single_launch, rcp_out_scale)
     if workspace_buffer is None:
         info = PlanInfo()
         _check(L.pkv_query_plan(ctypes.byref(d), num_kv_heads, page_size, sliding_win_size,
@@ -339,6 +335,59 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
             st = L.pkv_decode_attn(*args)
         else:
             st = L.pkv_decode_attn_ex(*args, ctypes.byref(opts))
+    _check(st)
+    return output
+
+
+def _decode_prep(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size,
+                 sinks, q_scale, kv_scale, kv_layout, q_seq_len, mask, head_dim_v, path,
+                 split_pages, target_ctas, split_event, single_launch, rcp_out_scale):
+    """Argument checks and the C structs of a decode call (no device work)."""
+    if q.device.type != "cuda":
+        raise PkvError(1, "decode_attn runs on the GPU only: q must be a device tensor")
+    _shape_checks(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size,
+                  kv_layout, q_seq_len, head_dim_v, mask)
+    if sinks is not None:
+        if sinks.dtype != torch.float32 or sinks.numel() != q.shape[-2] or not sinks.is_contiguous():
+            raise PkvError(1, "sinks must be contiguous float32 [num_kv_heads, head_group_ratio]")
+    ev = None if split_event is None else split_event.cuda_event
+    q_scale, q_scale_dev = _scale_arg(q_scale, "q_scale", q.device)
+    kv_scale, kv_scale_dev = _scale_arg(kv_scale, "kv_scale", q.device)
+    out_fp8 = output.dtype in (torch.float8_e4m3fn, torch.uint8)
+    opts = _options(path, split_pages, 0, target_ctas, ev, q_scale_dev, kv_scale_dev,
+                    single_launch, out_fp8, rcp_out_scale)
+    d = _dims(q, k_cache, page_table, head_dim_v, q_seq_len)
+    return opts, d, q_scale, kv_scale
+
+
+def decode_attn_noalloc(q, k_cache, v_cache, page_table, seq_lens, output, *, num_kv_heads,
+                        page_size, sinks=None, q_scale=1.0, kv_scale=1.0, sliding_win_size=0,
+                        kv_layout="NHD", q_seq_len=1, mask=None, head_dim_v=None, path=None,
+                        split_pages=0, target_ctas=0, stream=None, split_event=None,
+                        single_launch=None, rcp_out_scale=1.0):
+    """``decode_attn`` without a workspace and without allocating anything.
+
+    The partial results live in the library's static per-GPU scratch
+    (``pkv_decode_attn_noalloc``): calls that overlap in time on one GPU race,
+    and a plan needing more than ``NOALLOC_SCRATCH_BYTES`` raises.  Returns
+    ``output``.
+    """
+    if head_dim_v is None:
+        head_dim_v = output.shape[-1]
+    L = lib()
+    opts, d, q_scale, kv_scale = _decode_prep(
+        q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size, sinks,
+        q_scale, kv_scale, kv_layout, q_seq_len, mask, head_dim_v, path, split_pages,
+        target_ctas, split_event, single_launch, rcp_out_scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = L.pkv_decode_attn_noalloc(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), _ptr(output),
+            num_kv_heads, page_size, _LAYOUT[kv_layout], _ptr(sinks), float(q_scale),
+            float(kv_scale), int(sliding_win_size), int(q_seq_len),
+            _ptr(mask if q_seq_len > 1 else None), ctypes.c_void_p(stream), ctypes.byref(d),
+            None if opts is None else ctypes.byref(opts))
     _check(st)
     return output
 

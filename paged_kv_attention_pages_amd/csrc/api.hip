@@ -16,11 +16,19 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "../../include/pkv.h"
 #include "kernels.h"
+
+// Scratch memory of pkv_decode_attn_noalloc: a fixed array in device global
+// memory, one copy per GPU the library runs on, held until the process ends.
+// On the host this name stands for a host-side shadow, not a device address:
+// host code passes only the address hipGetSymbolAddress returns for the
+// current GPU (scratch_of_current_device below).
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -72,6 +80,32 @@ struct Plan {
 // Generation of a single-launch-merge call: tags the per-unit counters so
 // that words left by other calls count as zero.
 std::atomic<unsigned> g_gen{0};
+
+// Device address of `scratch` per GPU, looked up on the first no-alloc call
+// made with that GPU current.
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+pkv_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(PKV_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(PKV_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PKV_OK;
+}
 
 // Host-side checks shared by every entry point, then the plan.
 pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window, int Tq,
@@ -439,6 +473,36 @@ pkv_status pkv_decode_attn_ex(const void* q, const void* k_cache, const void* v_
   return decode(q, k_cache, v_cache, page_table, seq_lens, out, workspace, num_kv_heads,
                 page_size, layout, sinks, q_scale, kv_scale, window, q_seq_len, mask, stream,
                 dims, opts);
+}
+
+pkv_status pkv_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* page_table, const uint32_t* seq_lens,
+                                   void* out, int num_kv_heads, int page_size, int layout,
+                                   const float* sinks, float q_scale, float kv_scale, int window,
+                                   int q_seq_len, const uint16_t* mask, void* stream,
+                                   const pkv_dims* dims, const pkv_options* opts) {
+  if (dims == nullptr) return fail(PKV_ERR_INVALID_ARGUMENT, "dims is NULL");
+  // the same plan decode() makes, to size the scratch before any device call
+  Plan pl;
+  const bool aliased = v_cache != nullptr && v_cache == k_cache && dims->head_dim_v < dims->head_dim_qk;
+  pkv_status st = make_plan(dims, num_kv_heads, page_size, layout, window, q_seq_len, aliased,
+                            opts, &pl);
+  if (st != PKV_OK) return st;
+  if (pl.ws_bytes > PKV_NOALLOC_SCRATCH_BYTES)
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL,
+                "this call needs %zu bytes of scratch; pkv_decode_attn_noalloc has %zu "
+                "(call pkv_decode_attn_ex with a workspace instead)",
+                pl.ws_bytes, (size_t)PKV_NOALLOC_SCRATCH_BYTES);
+  if (dims->batch == 0) return PKV_OK;
+  void* ws = nullptr;
+  if (pl.ws_bytes > 0) {
+    st = scratch_of_current_device(&ws);
+    if (st != PKV_OK) return st;
+  }
+  pkv_dims d = *dims;
+  d.workspace_bytes = PKV_NOALLOC_SCRATCH_BYTES;
+  return decode(q, k_cache, v_cache, page_table, seq_lens, out, ws, num_kv_heads, page_size,
+                layout, sinks, q_scale, kv_scale, window, q_seq_len, mask, stream, &d, opts);
 }
 
 pkv_status pkv_validate_inputs(const int32_t* page_table, const uint32_t* seq_lens,

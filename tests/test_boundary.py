@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (pkv_\w+)", out))
     assert set(names) <= exported, set(names) - exported
-    assert pkv.lib().pkv_abi_version() == 6
+    assert pkv.lib().pkv_abi_version() == 7
 
 
 def test_struct_layouts_match_header(tmp_path):
