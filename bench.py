@@ -111,6 +111,8 @@ def main():
     ap.add_argument("--path", default=None, help="auto | valu | mfma | mfma_mla")
     ap.add_argument("--split-pages", type=int, default=0)
     ap.add_argument("--target-ctas", type=int, default=0)
+    ap.add_argument("--batch", type=int, default=0,
+                    help="number of sequences of the named decode workload (0: its own)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -144,7 +146,7 @@ def main():
     torch.cuda.set_device(dev)
     rec = measure_decode(args.workload, args, args.cpu_seconds, headline=True)
     if args.workload == "llama3_8b_gqa" and not args.no_configs and not (args.path or args.split_pages or
-                                                                          args.target_ctas):
+                                                                          args.target_ctas or args.batch):
         # every other decode configuration, measured in the same run
         cfgs = {}
         for name in ["tiny", "fp8_window_sinks", "spec_decode", "mla", "mla_fp8"]:
@@ -171,6 +173,8 @@ def measure_decode(name, args, cpu_budget, headline):
 
     dev = torch.device("cuda:0")
     w = synth.WORKLOADS[name]
+    if headline and args.batch:
+        w = w.replace(batch=args.batch)
     seed = SEEDS.get(name, 1)
     L = synth.draw_seq_lens(w, seed)
     kf = (L - w.q_seq_len + 1 - w.window).clamp(min=0) if w.window > 0 else None

@@ -236,7 +236,10 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
   const int64_t sk_tile = path == PKV_PATH_MFMA_MLA ? 32 : 16;
   const bool sk_path = (path == PKV_PATH_MFMA || path == PKV_PATH_MFMA_MLA) &&
                        units * (cdiv(pages_max * ps, sk_tile) + 1) < ((int64_t)1 << 31);
-  if (sk_path && d->batch <= 256 && !(opts && opts->split_pages > 0)) {
+  // (up to 256 sequences; the matrix-core kernel with head dims up to 128
+  // also has a wider schedule for up to 1024)
+  const int64_t sk_max_batch = path == PKV_PATH_MFMA && Dk <= 128 && Dv <= 128 ? 1024 : 256;
+  if (sk_path && d->batch <= sk_max_batch && !(opts && opts->split_pages > 0)) {
     // fp8 tiles carry half the bytes for the same matrix work, so more waves
     // per CU hide the conversion work: 8 per CU for fp8, 4 for 16-bit caches
     const int64_t per_cu = path == PKV_PATH_MFMA_MLA ? 1 : d->kv_dtype == PKV_FP8_E4M3 ? 8 : 4;

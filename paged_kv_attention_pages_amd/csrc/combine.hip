@@ -67,7 +67,7 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
 // hold 8 consecutive dims.  The slots are merged in chunks of 8 whose (m, l)
 // pairs and partial outputs are all loaded before any is used -- one memory
 // round trip per chunk -- with the running reference moved between chunks.
-template <int QT, int DV>
+template <int QT, int DV, int SC>
 __global__ __launch_bounds__(64) void combine_sk_kernel(Params p) {
   constexpr int LPR = DV / 8, RPW = 64 / LPR, CH = 8;
   resolve_scales(p);
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(64) void combine_sk_kernel(Params p) {
   const int r = blockIdx.x * RPW + lane / LPR;
   const bool row_ok = r < p.R;
   const int rr = row_ok ? r : 0;  // lanes past the last row read row 0 and store nothing
-  const SkSched S = sk_schedule(p);
+  const SkSchedC<SC> S = sk_schedule<SC>(p);
   const int W = sk_waves_eff(S.T, p.sk_waves);
   int pre, n;
   sk_seq_of(S, b, &pre, &n);
@@ -236,13 +236,19 @@ hipError_t launch_combine(int q_dtype, const Params& p, hipStream_t s) {
     return hipGetLastError();
   }
   if (p.sk_waves > 0) {
+    const bool wide = p.B > kSkMaxBatch;
+    if (p.B > kSkMaxBatchWide) return hipErrorInvalidValue;
 #define PKV_COMBINE_SK(DV)                                                                   \
   if (p.Dv == DV) {                                                                          \
     const dim3 ugrid((p.R + 64 / (DV / 8) - 1) / (64 / (DV / 8)), p.Hkv, p.B);              \
-    if (q_dtype == kBF16)                                                                    \
-      hipLaunchKernelGGL((combine_sk_kernel<kBF16, DV>), ugrid, dim3(64), 0, s, p);          \
+    if (q_dtype == kBF16 && !wide)                                                           \
+      hipLaunchKernelGGL((combine_sk_kernel<kBF16, DV, 4>), ugrid, dim3(64), 0, s, p);       \
+    else if (!wide)                                                                          \
+      hipLaunchKernelGGL((combine_sk_kernel<kF16, DV, 4>), ugrid, dim3(64), 0, s, p);        \
+    else if (q_dtype == kBF16)                                                               \
+      hipLaunchKernelGGL((combine_sk_kernel<kBF16, DV, 16>), ugrid, dim3(64), 0, s, p);      \
     else                                                                                     \
-      hipLaunchKernelGGL((combine_sk_kernel<kF16, DV>), ugrid, dim3(64), 0, s, p);           \
+      hipLaunchKernelGGL((combine_sk_kernel<kF16, DV, 16>), ugrid, dim3(64), 0, s, p);       \
     return hipGetLastError();                                                                \
   }
     PKV_COMBINE_SK(64)

@@ -128,26 +128,33 @@ __device__ __forceinline__ int wave_scan(int x) {
 // sequences and pre_b the tiles of the sequences before b.  Wave w of W takes
 // tiles [w T / W, (w+1) T / W), T = Hkv T1; when Hkv divides W, waves w and
 // w + k W / Hkv take the same tiles of KV heads kvh and kvh + k.
-// Lane l holds pre_b and n_b of sequences b = l + 64 c (c < 4: B <= 256).
+// Lane l holds pre_b and n_b of sequences b = l + 64 c, c < C (B <= 64 C):
+// C = 4 (up to 256 sequences) everywhere; the matrix-core kernel and its
+// combine also come with C = 16 (up to 1024 sequences, 32 more registers).
 constexpr int kSkMaxBatch = 256;
-struct SkSched {
+constexpr int kSkMaxBatchWide = 1024;
+template <int C>
+struct SkSchedC {
   int64_t T;     // total tiles
   int T1;        // tiles of one KV head
-  int pre[4];    // exclusive prefix of tiles per sequence (lane's sequences)
-  int cnt[4];    // tiles per sequence
+  int pre[C];    // exclusive prefix of tiles per sequence (lane's sequences)
+  int cnt[C];    // tiles per sequence
 };
+using SkSched = SkSchedC<4>;
 
 // First global tile of unit (b, kvh), given pre_b.
-__device__ __forceinline__ int64_t sk_unit_start(const SkSched& s, int kvh, int pre) {
+template <int C>
+__device__ __forceinline__ int64_t sk_unit_start(const SkSchedC<C>& s, int kvh, int pre) {
   return (int64_t)kvh * s.T1 + pre;
 }
 
-__device__ __forceinline__ SkSched sk_schedule(const Params& p) {
-  SkSched s;
+template <int C = 4>
+__device__ __forceinline__ SkSchedC<C> sk_schedule(const Params& p) {
+  SkSchedC<C> s;
   const int lane = threadIdx.x & 63;
   int carry = 0;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < C; ++c) {
     const int b = lane + 64 * c;
     int t0;
     const int n = (64 * c < p.B && b < p.B) ? seq_tiles(p, b, &t0) : 0;
@@ -188,24 +195,29 @@ struct SkUnit {
 // pre_b and n_b of sequence b (wave-uniform b): read every chunk's lane and
 // select on the scalar side, so the per-lane arrays are never indexed
 // dynamically (which would put them in scratch memory).
-__device__ __forceinline__ void sk_seq_of(const SkSched& s, int b, int* pre, int* n) {
+template <int C>
+__device__ __forceinline__ void sk_seq_of(const SkSchedC<C>& s, int b, int* pre, int* n) {
   const int ln = b & 63, c = b >> 6;
-  const int p0 = __builtin_amdgcn_readlane(s.pre[0], ln), p1 = __builtin_amdgcn_readlane(s.pre[1], ln);
-  const int p2 = __builtin_amdgcn_readlane(s.pre[2], ln), p3 = __builtin_amdgcn_readlane(s.pre[3], ln);
-  const int n0 = __builtin_amdgcn_readlane(s.cnt[0], ln), n1 = __builtin_amdgcn_readlane(s.cnt[1], ln);
-  const int n2 = __builtin_amdgcn_readlane(s.cnt[2], ln), n3 = __builtin_amdgcn_readlane(s.cnt[3], ln);
-  *pre = c == 0 ? p0 : c == 1 ? p1 : c == 2 ? p2 : p3;
-  *n = c == 0 ? n0 : c == 1 ? n1 : c == 2 ? n2 : n3;
+  int pr = 0, nn = 0;
+#pragma unroll
+  for (int k = 0; k < C; ++k) {
+    const int pk = __builtin_amdgcn_readlane(s.pre[k], ln), nk = __builtin_amdgcn_readlane(s.cnt[k], ln);
+    pr = c == k ? pk : pr;
+    nn = c == k ? nk : nn;
+  }
+  *pre = pr;
+  *n = nn;
 }
 
-__device__ __forceinline__ SkUnit sk_locate(const Params& p, const SkSched& s, int64_t x) {
+template <int C>
+__device__ __forceinline__ SkUnit sk_locate(const Params& p, const SkSchedC<C>& s, int64_t x) {
   SkUnit u;
   u.kvh = (int)(x / s.T1);
   const int xr = (int)(x - (int64_t)u.kvh * s.T1);
   // last sequence whose first tile is <= xr (it has tiles, since xr < T1)
   int best = 0;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < C; ++c) {
     const int b = (threadIdx.x & 63) + 64 * c;
     const bool ok = b < p.B && s.pre[c] <= xr;
     const uint64_t m = __ballot(ok);

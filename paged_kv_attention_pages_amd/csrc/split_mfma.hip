@@ -450,7 +450,8 @@ __device__ __forceinline__ void merge_unit(const Params& p, const Pending& u) {
 
 // Zero the outputs of the sequences with no visible token (they have no
 // tiles, so no wave meets them): wave w takes sequences w, w + W, ...
-__device__ __forceinline__ void zero_empty_units(const Params& p, const SkSched& S, int w, int W) {
+template <int SC>
+__device__ __forceinline__ void zero_empty_units(const Params& p, const SkSchedC<SC>& S, int w, int W) {
   const int lane = threadIdx.x & 63;
   for (int b = w; b < p.B; b += W) {
     int pre, n;
@@ -501,13 +502,14 @@ __global__ __launch_bounds__(64) void split_mfma16_kernel(Params p) {
 // p.fused the wave that completes a cut unit merges it (see merge_unit);
 // otherwise the combine kernel does.
 // FUSED selects the single-launch merge at compile time, so the two-launch
-// kernel carries none of its code or registers.
-template <int QT, int KT, int D, bool FUSED>
+// kernel carries none of its code or registers; SC is the schedule's chunk
+// count (4: up to 256 sequences, 16: up to 1024).
+template <int QT, int KT, int D, bool FUSED, int SC>
 // (two waves per SIMD: the register budget keeps the accumulators in
 // architected VGPRs instead of moving them through AGPRs every tile)
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma16_sk_kernel(Params p) {
   resolve_scales(p);
-  const SkSched S = sk_schedule(p);
+  const SkSchedC<SC> S = sk_schedule<SC>(p);
   const int W = sk_waves_eff(S.T, p.sk_waves);
   // workgroup (head group hg, position j) of sk_hb waves: wave i takes share
   // j of KV head hg * sk_hb + i's part of the tile stream (W / Hkv waves per
@@ -571,10 +573,20 @@ template <int QT, int KT, int D>
 hipError_t launch_split_mfma16(const Params& p, hipStream_t stream) {
   if (p.sk_waves > 0) {
     const dim3 grid(p.sk_waves / p.sk_hb), block(64 * p.sk_hb);
-    if (p.fused)
-      hipLaunchKernelGGL((split_mfma16_sk_kernel<QT, KT, D, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((split_mfma16_sk_kernel<QT, KT, D, false>), grid, block, 0, stream, p);
+    if (p.B <= kSkMaxBatch) {
+      if (p.fused)
+        hipLaunchKernelGGL((split_mfma16_sk_kernel<QT, KT, D, true, 4>), grid, block, 0, stream, p);
+      else
+        hipLaunchKernelGGL((split_mfma16_sk_kernel<QT, KT, D, false, 4>), grid, block, 0, stream, p);
+    } else if constexpr (D <= 128) {
+      // the wide schedule's registers fit beside head dims up to 128 only
+      if (p.fused)
+        hipLaunchKernelGGL((split_mfma16_sk_kernel<QT, KT, D, true, 16>), grid, block, 0, stream, p);
+      else
+        hipLaunchKernelGGL((split_mfma16_sk_kernel<QT, KT, D, false, 16>), grid, block, 0, stream, p);
+    } else {
+      return hipErrorInvalidValue;
+    }
   } else {
     dim3 grid(p.max_splits, p.Hkv, p.B);
     hipLaunchKernelGGL((split_mfma16_kernel<QT, KT, D>), grid, dim3(64), 0, stream, p);
@@ -584,7 +596,7 @@ hipError_t launch_split_mfma16(const Params& p, hipStream_t stream) {
 
 hipError_t launch_split_mfma16(int q_dtype, int kv_dtype, int D, const Params& p, hipStream_t s) {
   if (p.sk_waves == 0 && p.split_pages > 64) return hipErrorInvalidValue;
-  if (p.sk_waves > 0 && p.B > kSkMaxBatch) return hipErrorInvalidValue;
+  if (p.sk_waves > 0 && p.B > kSkMaxBatchWide) return hipErrorInvalidValue;
   if (p.sk_waves > 0 && (p.sk_hb < 1 || p.sk_hb > 8 || p.sk_waves % p.sk_hb ||
                          (p.sk_hb > 1 && (p.sk_waves % p.Hkv || p.Hkv % p.sk_hb))))
     return hipErrorInvalidValue;

@@ -123,8 +123,15 @@ def test_plan_stream_k():
     assert p["split_pages"] == 0 and p["ctas_per_split_grid"] == 4 * 256
     assert p["workspace_bytes"] >= 2 * 1024 * 4 * (128 * 4 + 8)
     assert plan(target_ctas=100)["ctas_per_split_grid"] == 100
-    # batches above 256 fall back to the grid schedule
-    assert plan(batch=300)["split_pages"] > 0
+    # the matrix-core schedule runs up to 1024 sequences (head dims <= 128),
+    # beyond that the grid schedule; head dim 256 and the latent path stop at 256
+    assert plan(batch=300)["split_pages"] == 0
+    assert plan(batch=1024)["split_pages"] == 0
+    assert plan(batch=1025)["split_pages"] > 0
+    assert plan(batch=300, head_dim_qk=256, head_dim_v=256)["split_pages"] > 0
+    lat = dict(num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512)
+    assert plan(batch=256, **lat)["split_pages"] == 0
+    assert plan(batch=257, **lat)["split_pages"] > 0
 
 
 def test_plan_stream_k_tile_count_edge():
@@ -180,7 +187,7 @@ def test_plan_single_launch_merge():
     assert plan()["single_launch"] == 0                       # 8 K tokens: two launches
     assert plan(pages_per_seq=2)["single_launch"] == 1        # 128 tokens: one launch
     assert plan(pages_per_seq=4, target_ctas=64)["single_launch"] == 0
-    assert plan(batch=300, single_launch=True)["single_launch"] == 0
+    assert plan(batch=1100, single_launch=True)["single_launch"] == 0
     assert plan(split_pages=4, single_launch=True)["single_launch"] == 0
     mla = plan(batch=32, num_q_heads=64, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
                pages_per_seq=256, single_launch=True)

@@ -342,6 +342,21 @@ def test_full_size_sampled_parity(name):
     assert not torch.isnan(got).any()
 
 
+def test_full_size_sampled_parity_512_sequences():
+    # the Llama-3-8B decode shape at 512 sequences: the wide stream-K schedule
+    w = synth.WORKLOADS["llama3_8b_gqa"].replace(batch=512)
+    print("[case] full llama3_8b_gqa batch 512", flush=True)
+    inp = make(w, seed=2)
+    plan = pkv.query_plan(batch=512, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                          head_dim_qk=128, head_dim_v=128, pages_per_seq=inp["page_table"].shape[1],
+                          page_size=w.page_size)
+    assert plan["split_pages"] == 0
+    got = run_gpu(w, inp)
+    idx = _sample(inp["seq_lens_host"], 6)
+    assert_parity(w, got[idx.to(DEV)], run_oracle(w, inp, idx), "full/gqa-b512")
+    assert not torch.isnan(got).any()
+
+
 # ---------------------------------------------------------------- exact visible sets
 
 def _probe(w, inp):
@@ -662,20 +677,52 @@ def test_mla_stream_k_workgroup_counts(W):
 
 # ---------------------------------------------------------------- schedules and capture
 
-@pytest.mark.parametrize("name", ["gqa", "mla"])
-def test_batch_above_256_uses_split_grid(name):
-    # the stream-K schedule keeps per-sequence prefix sums for <= 256
-    # sequences; larger batches take the split grid
-    w = (SMALL["gqa"] if name == "gqa" else MLA_SMALL).replace(batch=300, seq_len_range=(0, 200))
-    print(f"[case] batch 300 {name}", flush=True)
+@pytest.mark.parametrize("name,B", [("gqa", 1100), ("mla", 300)])
+def test_batch_above_schedule_limit_uses_split_grid(name, B):
+    # the stream-K schedule keeps per-sequence prefix sums for up to 1024
+    # sequences (matrix-core path) or 256 (latent path); larger batches take
+    # the split grid
+    w = (SMALL["gqa"] if name == "gqa" else MLA_SMALL).replace(batch=B, seq_len_range=(0, 200))
+    print(f"[case] batch {B} {name}", flush=True)
     inp = make(w, seed=98)
-    plan = pkv.query_plan(batch=300, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+    plan = pkv.query_plan(batch=B, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                           head_dim_qk=w.head_dim_qk, head_dim_v=w.head_dim_v,
                           pages_per_seq=inp["page_table"].shape[1], page_size=w.page_size,
                           q_dtype=w.q_dtype, kv_dtype=w.kv_dtype)
     assert plan["max_splits"] > 0  # grid schedule
     got = run_gpu(w, inp)
-    assert_parity(w, got, run_oracle(w, inp), f"batch300/{name}")
+    assert_parity(w, got, run_oracle(w, inp), f"batch{B}/{name}")
+
+
+@pytest.mark.parametrize("B", [257, 512, 1024])
+@pytest.mark.parametrize("kind", ["gqa", "fp8", "spec", "gqa_single_launch", "d64"])
+def test_stream_k_wide_batches(kind, B):
+    # more than 256 sequences: the matrix-core kernel and its combine run the
+    # 16-chunk schedule (lanes hold the prefix sums of 16 sequences each);
+    # lengths from 0 give empty sequences, which must come out as zeros
+    base = {"gqa": SMALL["gqa"], "fp8": SMALL["fp8"], "spec": SMALL["spec"],
+            "gqa_single_launch": SMALL["gqa"],
+            "d64": SMALL["gqa"].replace(head_dim_qk=64, head_dim_v=64)}[kind]
+    w = base.replace(batch=B, seq_len_range=(4, 300))
+    kw = {"single_launch": True} if kind == "gqa_single_launch" else {}
+    print(f"[case] stream-K batch {B} {kind}", flush=True)
+    L = synth.draw_seq_lens(w, 100 + B)
+    if kind != "spec":          # (drafts need q_seq_len <= seq_len)
+        L[::97] = 0
+    inp = make(w, seed=100 + B, seq_lens=L)
+    plan = pkv.query_plan(batch=B, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                          head_dim_qk=w.head_dim_qk, head_dim_v=w.head_dim_v,
+                          pages_per_seq=inp["page_table"].shape[1], page_size=w.page_size,
+                          q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, window=w.window,
+                          q_seq_len=w.q_seq_len, **kw)
+    assert plan["split_pages"] == 0 and plan["max_splits"] == 0  # stream-K
+    got = run_gpu(w, inp, **kw)
+    ref = run_oracle(w, inp)
+    assert_parity(w, got, ref, f"sk-wide/{kind}/B{B}")
+    if kind != "spec":
+        L = inp["seq_lens"].cpu()
+        assert bool((L == 0).any())
+        assert torch.equal(got[L == 0].float().cpu(), torch.zeros_like(got[L == 0].float().cpu()))
 
 
 @pytest.mark.parametrize("name", ["gqa", "spec", "mla"])
