@@ -114,10 +114,13 @@ typedef struct pkv_dims {
   uint64_t workspace_bytes; /* size of the caller's workspace buffer        */
 } pkv_dims;
 
-/* Kernel paths.  PKV_PATH_AUTO lets the planner choose. */
+/* Kernel paths.  PKV_PATH_AUTO lets the planner choose.  PKV_PATH_VALU is a
+ * non-default reference path: the planner never picks it (the matrix-core
+ * kernel, with its rows padded to 16, is faster at every measured shape,
+ * small groups included); it runs only when forced, on the split grid. */
 typedef enum {
   PKV_PATH_AUTO = 0,
-  PKV_PATH_VALU = 1,      /* vector-ALU dot products, rows < 16             */
+  PKV_PATH_VALU = 1,      /* vector-ALU dot products, head dim 128, <= 8 rows */
   PKV_PATH_MFMA = 2,      /* matrix-core tiles, up to 16 rows per KV head   */
   PKV_PATH_MFMA_MLA = 3   /* matrix-core, 64 rows, latent (aliased) cache   */
 } pkv_path;
