@@ -1,6 +1,6 @@
 """Benchmark: paged GQA decode attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--batch B]
 
 A step is one decode call (split-KV kernel + combine kernel) over one batch
 of the workload, with every input already resident in HBM.  The default
@@ -20,6 +20,8 @@ Reported (one JSON line on stdout):
                bytes per launch / its mean time, against the HBM peak
   cpu_baseline the fp64 oracle on a bounded sample of the same batch, on the
                host cores (a reported baseline, not the target)
+  host_us_per_call  the host side of a call (binding + launch), each call
+               timed alone after a synchronisation, median of up to 100
   configs      (default run) the other decode configurations measured the same
                way in the same run -- tiny, fp8 + window + sinks, speculative
                decode, latent (MLA) and its fp8 form: us/call, effective GB/s,
@@ -239,11 +241,22 @@ def measure_decode(name, args, cpu_budget, headline):
     split_ms = [ev_s[i].elapsed_time(ev_m[i]) for i in range(K)]
     comb_ms = [ev_m[i].elapsed_time(ev_e[i]) for i in range(K)]
     split_mean = statistics.fmean(split_ms)
+    # pass 3 -- the host side: each call timed alone on the host after a
+    # synchronisation (binding + launch, with an empty launch queue)
+    host = []
+    for i in range(min(K, 100)):
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        call(i)
+        host.append(time.perf_counter() - h0)
+    torch.cuda.synchronize()
+    host_us = statistics.median(host) * 1e6
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (split_mean * 1e-3) / 1e9
     print(f"[bench] {w.name}: {ms_per_step * 1e3:.1f} us/call wall, evented pass: call median "
           f"{statistics.median(call_ms) * 1e3:.1f} us (split {split_mean * 1e3:.1f} us, combine "
-          f"{statistics.fmean(comb_ms) * 1e3:.1f} us), {value:.0f} GB/s effective, plan {plan}",
+          f"{statistics.fmean(comb_ms) * 1e3:.1f} us), host {host_us:.1f} us per call, "
+          f"{value:.0f} GB/s effective, plan {plan}",
           file=sys.stderr, flush=True)
 
     cpu = None
@@ -276,6 +289,7 @@ def measure_decode(name, args, cpu_budget, headline):
             "split_us_mean": round(split_mean * 1e3, 2),
             "split_frac_hbm_peak": round(achieved / HBM_PEAK_GBS, 4),
             "combine_us_mean": round(statistics.fmean(comb_ms) * 1e3, 2),
+            "host_us_per_call": round(host_us, 2),
             "traffic": traffic, "cpu_baseline": cpu,
         }
         if path == "mfma_mla":
@@ -292,6 +306,7 @@ def measure_decode(name, args, cpu_budget, headline):
         "us_per_call": round(ms_per_step * 1e3, 2),
         "us_per_call_evented_median": round(statistics.median(call_ms) * 1e3, 2),
         "us_per_call_evented_p10_p90": [round(q * 1e3, 2) for q in _p10_p90(call_ms)],
+        "host_us_per_call": round(host_us, 2),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "config": cfg,
         "roofline": {

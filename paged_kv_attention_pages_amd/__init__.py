@@ -50,6 +50,8 @@ class Dims(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_uint64)]
 
 
+PKV_ERR_WORKSPACE_TOO_SMALL = 3
+
 # bytes of the static per-GPU scratch of pkv_decode_attn_noalloc
 NOALLOC_SCRATCH_BYTES = 96 << 20
 
@@ -146,7 +148,26 @@ def _check(status: int):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: ctypes converts it for c_void_p arguments
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _current_stream(dev: int) -> int:
+    """Handle of torch's current stream on device index `dev`."""
+    if _raw_stream is not None:
+        return _raw_stream(dev)
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _call_on(dev: int, fn, *args):
+    """fn(*args) with device `dev` current (switching only when it is not)."""
+    if torch.cuda.current_device() == dev:
+        return fn(*args)
+    with torch.cuda.device(dev):
+        return fn(*args)
 
 
 def _dims(q, k_cache, page_table, head_dim_v, q_seq_len, workspace_bytes=0) -> Dims:
@@ -277,12 +298,13 @@ def _shape_checks(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_head
         want = (B, q_seq_len, ((q_seq_len + 31) // 32) * 2)
         if mask.dtype not in (torch.uint16, torch.int16) or tuple(mask.shape) != want:
             raise PkvError(1, f"mask must be uint16 {want}, got {mask.dtype} {tuple(mask.shape)}")
+    dev = q.get_device()
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                     ("page_table", page_table), ("seq_lens", seq_lens), ("output", output),
                     ("mask", mask)):
         if t is not None and not t.is_contiguous():
             raise PkvError(1, f"{name} must be contiguous")
-        if t is not None and t.device != q.device:
+        if t is not None and (not t.is_cuda or t.get_device() != dev):
             raise PkvError(1, f"{name} is on {t.device}, q on {q.device}")
 
 
@@ -314,27 +336,31 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
         q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size, sinks,
         q_scale, kv_scale, kv_layout, q_seq_len, mask, head_dim_v, path, split_pages,
         target_ctas, split_event, single_launch, rcp_out_scale)
-    if workspace_buffer is None:
-        info = PlanInfo()
-        _check(L.pkv_query_plan(ctypes.byref(d), num_kv_heads, page_size, sliding_win_size,
-                                q_seq_len, None if opts is None else ctypes.byref(opts),
-                                ctypes.byref(info)))
-        if stream is None:
-            stream = torch.cuda.current_stream(q.device).cuda_stream
-        workspace_buffer = _workspace(q.device, stream, info.workspace_bytes)
-    d.workspace_bytes = workspace_buffer.numel() * workspace_buffer.element_size()
+    dev = q.get_device()
     if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    with torch.cuda.device(q.device):
+        stream = _current_stream(dev)
+    own_ws = workspace_buffer is None
+    if own_ws:
+        # the stream's cached workspace; the library rejects it (before any
+        # device work) when this call needs more, and it is grown then
+        workspace_buffer = _workspace(q.device, stream, 0)
+    fn = L.pkv_decode_attn if opts is None else L.pkv_decode_attn_ex
+    extra = () if opts is None else (ctypes.byref(opts),)
+    for attempt in (0, 1):
+        d.workspace_bytes = workspace_buffer.numel() * workspace_buffer.element_size()
         args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens),
                 _ptr(output), _ptr(workspace_buffer), num_kv_heads, page_size, _LAYOUT[kv_layout],
                 _ptr(sinks), float(q_scale), float(kv_scale), int(sliding_win_size),
-                int(q_seq_len), _ptr(mask if q_seq_len > 1 else None), ctypes.c_void_p(stream),
-                ctypes.byref(d))
-        if opts is None:
-            st = L.pkv_decode_attn(*args)
-        else:
-            st = L.pkv_decode_attn_ex(*args, ctypes.byref(opts))
+                int(q_seq_len), _ptr(mask if q_seq_len > 1 else None), stream,
+                ctypes.byref(d)) + extra
+        st = _call_on(dev, fn, *args)
+        if st != PKV_ERR_WORKSPACE_TOO_SMALL or not own_ws or attempt:
+            break
+        info = PlanInfo()
+        _check(_call_on(dev, L.pkv_query_plan, ctypes.byref(d), num_kv_heads, page_size,
+                        sliding_win_size, q_seq_len, None if opts is None else ctypes.byref(opts),
+                        ctypes.byref(info)))
+        workspace_buffer = _workspace(q.device, stream, info.workspace_bytes)
     _check(st)
     return output
 
@@ -343,7 +369,7 @@ def _decode_prep(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads
                  sinks, q_scale, kv_scale, kv_layout, q_seq_len, mask, head_dim_v, path,
                  split_pages, target_ctas, split_event, single_launch, rcp_out_scale):
     """Argument checks and the C structs of a decode call (no device work)."""
-    if q.device.type != "cuda":
+    if not q.is_cuda:
         raise PkvError(1, "decode_attn runs on the GPU only: q must be a device tensor")
     _shape_checks(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size,
                   kv_layout, q_seq_len, head_dim_v, mask)
@@ -379,15 +405,15 @@ def decode_attn_noalloc(q, k_cache, v_cache, page_table, seq_lens, output, *, nu
         q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size, sinks,
         q_scale, kv_scale, kv_layout, q_seq_len, mask, head_dim_v, path, split_pages,
         target_ctas, split_event, single_launch, rcp_out_scale)
+    dev = q.get_device()
     if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    with torch.cuda.device(q.device):
-        st = L.pkv_decode_attn_noalloc(
-            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), _ptr(output),
-            num_kv_heads, page_size, _LAYOUT[kv_layout], _ptr(sinks), float(q_scale),
-            float(kv_scale), int(sliding_win_size), int(q_seq_len),
-            _ptr(mask if q_seq_len > 1 else None), ctypes.c_void_p(stream), ctypes.byref(d),
-            None if opts is None else ctypes.byref(opts))
+        stream = _current_stream(dev)
+    st = _call_on(dev, L.pkv_decode_attn_noalloc,
+                  _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens),
+                  _ptr(output), num_kv_heads, page_size, _LAYOUT[kv_layout], _ptr(sinks),
+                  float(q_scale), float(kv_scale), int(sliding_win_size), int(q_seq_len),
+                  _ptr(mask if q_seq_len > 1 else None), stream, ctypes.byref(d),
+                  None if opts is None else ctypes.byref(opts))
     _check(st)
     return output
 
