@@ -170,15 +170,19 @@ __device__ __forceinline__ void compute_tile(const Params& p, const SeqGeom& sg,
   // ---- O^T += V^T . P^T
   // operand of dim j: element j of the lane's V chunk for its four tokens
   if constexpr (KT == kFP8) {
-    // gather byte j of the four tokens into one word, convert the four at
-    // once (exact), and keep them in token order
+    // dims j and j + 1 (bytes b, b + 1 of a word) of two tokens: one byte
+    // permute per token pair puts [t0 b, t1 b, t0 b+1, t1 b+1] in a word,
+    // whose low and high byte pairs convert (exactly) to the (t0, t1)
+    // operand halves of the two dims
 #pragma unroll
-    for (int j = 0; j < DT; ++j) {
+    for (int j = 0; j < DT; j += 2) {
       const int wi = j >> 2, b = j & 3;
-      const uint32_t p01 = __builtin_amdgcn_perm(T.v[1][wi], T.v[0][wi], 0x0c0c0400u | (b << 8) | b);
-      const uint32_t p23 = __builtin_amdgcn_perm(T.v[3][wi], T.v[2][wi], 0x04000c0cu | (b << 24) | (b << 16));
-      const uint2 a = fp8x4_to_16<QT>(p01 | p23);
-      A.o[j] = mfma_k16<QT>(a, pb, A.o[j]);
+      const uint32_t sel = (uint32_t)b | ((uint32_t)(b + 4) << 8) | ((uint32_t)(b + 1) << 16) |
+                           ((uint32_t)(b + 5) << 24);
+      const uint2 c01 = fp8x4_to_16<QT>(__builtin_amdgcn_perm(T.v[1][wi], T.v[0][wi], sel));
+      const uint2 c23 = fp8x4_to_16<QT>(__builtin_amdgcn_perm(T.v[3][wi], T.v[2][wi], sel));
+      A.o[j] = mfma_k16<QT>(make_uint2(c01.x, c23.x), pb, A.o[j]);
+      A.o[j + 1] = mfma_k16<QT>(make_uint2(c01.y, c23.y), pb, A.o[j + 1]);
     }
   } else {
     // element j of tokens 0, 1 (2, 3) into one word with one byte permute:
