@@ -312,7 +312,7 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
                 num_kv_heads, page_size, sinks=None, q_scale=1.0, kv_scale=1.0,
                 sliding_win_size=0, kv_layout="NHD", q_seq_len=1, mask=None, head_dim_v=None,
                 path=None, split_pages=0, target_ctas=0, stream=None, split_event=None,
-                single_launch=None, rcp_out_scale=1.0):
+                single_launch=None, rcp_out_scale=1.0, num_cus=0):
     """Paged-KV decode attention, written in place into ``output``.
 
     q [B, q_seq_len, Hq, Dqk] (or [B, Hq, Dqk], or the xqa page's beam-1
@@ -327,7 +327,8 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
     makes the matrix-core stream-K plan merge cut units in the split kernel
     (True) or in a second kernel (False).  A float8_e4m3fn ``output`` (fp8
     caches only, as the xqa page allows the cache's dtype) receives
-    round(out * rcp_out_scale).  Returns ``output``.
+    round(out * rcp_out_scale).  ``num_cus`` (0: the device's) is the CU
+    count the planner sizes the schedule for.  Returns ``output``.
     """
     if head_dim_v is None:
         head_dim_v = output.shape[-1]
@@ -335,7 +336,7 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
     opts, d, q_scale, kv_scale = _decode_prep(
         q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size, sinks,
         q_scale, kv_scale, kv_layout, q_seq_len, mask, head_dim_v, path, split_pages,
-        target_ctas, split_event, single_launch, rcp_out_scale)
+        target_ctas, split_event, single_launch, rcp_out_scale, num_cus)
     dev = q.get_device()
     if stream is None:
         stream = _current_stream(dev)
@@ -367,7 +368,7 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
 
 def _decode_prep(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size,
                  sinks, q_scale, kv_scale, kv_layout, q_seq_len, mask, head_dim_v, path,
-                 split_pages, target_ctas, split_event, single_launch, rcp_out_scale):
+                 split_pages, target_ctas, split_event, single_launch, rcp_out_scale, num_cus=0):
     """Argument checks and the C structs of a decode call (no device work)."""
     if not q.is_cuda:
         raise PkvError(1, "decode_attn runs on the GPU only: q must be a device tensor")
@@ -380,7 +381,7 @@ def _decode_prep(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads
     q_scale, q_scale_dev = _scale_arg(q_scale, "q_scale", q.device)
     kv_scale, kv_scale_dev = _scale_arg(kv_scale, "kv_scale", q.device)
     out_fp8 = output.dtype in (torch.float8_e4m3fn, torch.uint8)
-    opts = _options(path, split_pages, 0, target_ctas, ev, q_scale_dev, kv_scale_dev,
+    opts = _options(path, split_pages, num_cus, target_ctas, ev, q_scale_dev, kv_scale_dev,
                     single_launch, out_fp8, rcp_out_scale)
     d = _dims(q, k_cache, page_table, head_dim_v, q_seq_len)
     return opts, d, q_scale, kv_scale

@@ -74,6 +74,7 @@ struct Plan {
   size_t ws_cnt_off;   // offset of the per-unit counters (single-launch merge)
   bool fused;          // cut units merged in the split kernel (no combine launch)
   bool lat_ws;         // latent stream-K with separate score / P.V waves (16-bit cache)
+  bool unit_aligned;   // matrix-core stream-K over B * Hkv waves, one per unit when even
   size_t ws_bytes;
 };
 
@@ -222,6 +223,7 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
   pl->sk_hb = 1;
   pl->fused = false;
   pl->lat_ws = false;
+  pl->unit_aligned = false;
   pl->ws_cnt_off = 0;
   // Stream-K schedule (matrix-core path, batch <= 256, no forced split size):
   // persistent waves (measured best: one per SIMD for 16-bit caches, each
@@ -275,6 +277,33 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
     // it is used when no wave's share can exceed 8 tiles.  The latent-cache
     // kernel leaves the merge of its 64-row partials to the combine kernel.
     const int mode = opts ? opts->merge_mode : 0;
+    // With a window every unit spans at most cdiv(window + Tq - 1, 16) + 1
+    // tiles, and where the sequences reach past the window the units are of
+    // (nearly) equal length.  Then one wave per whole unit is as balanced as
+    // equal shares, cuts nothing and leaves the merge pass nothing to do
+    // (measured, fp8 + window 4096 + sinks, 1024 units of 4096 tokens: the
+    // call 200 -> 182 us).  The plan launches B * Hkv waves and workspace for
+    // equal shares over them; the kernels choose between the two on the
+    // device, from the lengths (sk_units_even), so a batch of mostly short
+    // sequences still gets equal shares.  Used by default when the units give
+    // every CU at least two waves.
+    if (path == PKV_PATH_MFMA && window > 0 && mode == 0 && !(opts && opts->target_ctas > 0) &&
+        units >= 2 * (int64_t)cus && units <= (1 << 20)) {
+      pl->unit_aligned = true;
+      pl->sk_waves = (int)units;
+      pl->sk_hb = 1;
+      const int64_t res = std::min<int64_t>(8, units / cus);
+      for (int h = (int)std::min<int64_t>(res, Hkv); h > 1; --h)
+        if (Hkv % h == 0) {
+          pl->sk_hb = h;
+          break;
+        }
+      const size_t nrow_u = (size_t)2 * pl->sk_waves * R;
+      pl->ws_o_bytes = nrow_u * Dv * sizeof(float);
+      pl->ws_ml_off = (pl->ws_o_bytes + 255) & ~(size_t)255;
+      pl->ws_bytes = pl->ws_ml_off + nrow_u * 2 * sizeof(float);
+      return PKV_OK;
+    }
     const int64_t max_tiles = units * cdiv(pages_max * ps, 16);
     pl->fused = path == PKV_PATH_MFMA &&
                 (mode == 2 || (mode == 0 && max_tiles <= 8 * (int64_t)pl->sk_waves));
@@ -382,6 +411,7 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
   p.qk_unit = (float)(1.4426950408889634 / std::sqrt((double)Dk));
   p.fused = pl.fused ? 1 : 0;
   p.ws_lanes = pl.lat_ws ? 1 : 0;
+  p.sk_units = pl.unit_aligned ? 1 : 0;
   p.out_fp8 = out_fp8 ? 1 : 0;
   p.rcp_out_scale = rcp_out;
   p.ws_cnt = pl.fused ? (unsigned long long*)((char*)workspace + pl.ws_cnt_off) : nullptr;

@@ -62,7 +62,8 @@ __global__ __launch_bounds__(64) void combine_kernel(Params p) {
 // span more than one wave's share.  Wave w0 left its piece in slot 2 w0 (when
 // the unit is its first) or 2 w0 + 1 (its last); every later wave up to w1
 // has the unit first and left slot 2 w.  Units held by one wave were finished
-// by the split kernel; units with no tiles get zeros here.
+// by the split kernel; units with no tiles get zeros here.  Under the
+// one-wave-per-unit plan with even units nothing was cut and every wave exits.
 // One wave per (unit, group of 64 / (DV / 8) rows): each row's DV / 8 lanes
 // hold 8 consecutive dims.  The slots are merged in chunks of 8 whose (m, l)
 // pairs and partial outputs are all loaded before any is used -- one memory
@@ -77,6 +78,8 @@ __global__ __launch_bounds__(64) void combine_sk_kernel(Params p) {
   const bool row_ok = r < p.R;
   const int rr = row_ok ? r : 0;  // lanes past the last row read row 0 and store nothing
   const SkSchedC<SC> S = sk_schedule<SC>(p);
+  // the split kernel gave every unit a wave of its own: nothing was cut
+  if (p.sk_units && sk_units_even(p, S)) return;
   const int W = sk_waves_eff(S.T, p.sk_waves);
   int pre, n;
   sk_seq_of(S, b, &pre, &n);

@@ -54,6 +54,10 @@ struct Params {
   // latent stream-K partials in the P.V waves' register order, 64 rows a
   // slot (split_mla_ws.hip; merged by combine_lat_kernel)
   int ws_lanes;
+  // matrix-core stream-K over sk_waves == B * Hkv waves that, when the units
+  // are even (sk_units_even), give each unit one wave and cut nothing (the
+  // combine then finds nothing to merge); otherwise equal shares as usual
+  int sk_units;
 };
 
 // Scales from device memory when the call passed them there: every kernel
@@ -183,6 +187,22 @@ __device__ __forceinline__ int64_t sk_wave_start(int64_t T, int w, int W) {
 // The wave whose range holds global tile x: the largest w with start(w) <= x.
 __device__ __forceinline__ int sk_wave_of(int64_t T, int64_t x, int W) {
   return (int)(((x + 1) * (int64_t)W + T - 1) / T) - 1;
+}
+
+// Whether the units are even enough to give each its own wave: the longest
+// unit's tiles times the unit count within 5/4 of all tiles, i.e. one wave
+// per unit takes at most a quarter longer than equal shares of the same
+// tiles (which pay for their cuts and a merge pass instead).  Empty units
+// count, as waves with nothing to do.  Wave-uniform.
+template <int C>
+__device__ __forceinline__ bool sk_units_even(const Params& p, const SkSchedC<C>& s) {
+  int mx = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) mx = max(mx, s.cnt[c]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mx = max(mx, __shfl_xor(mx, d));
+  mx = __builtin_amdgcn_readfirstlane(mx);
+  return 4 * (int64_t)mx * p.B <= 5 * (int64_t)s.T1;
 }
 
 // Unit holding global tile x (x < T): sequence b, KV head kvh, its first

@@ -452,6 +452,15 @@ __device__ __forceinline__ void merge_unit(const Params& p, const Pending& u) {
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Zero the outputs of one (sequence, KV head) unit's rows.
+__device__ __forceinline__ void zero_unit(const Params& p, int b, int kvh) {
+  const int lane = threadIdx.x & 63;
+  for (int r = 0; r < p.R; ++r) {
+    const int64_t ob = q_row_offset(p, b, kvh, r) * p.Dv;
+    for (int d = 4 * lane; d < p.Dv; d += 256) store_out4<kBF16>(p, ob + d, 0.f, 0.f, 0.f, 0.f);
+  }
+}
+
 // Zero the outputs of the sequences with no visible token (they have no
 // tiles, so no wave meets them): wave w takes sequences w, w + W, ...
 template <int SC>
@@ -528,8 +537,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   // registers (a value derived from threadIdx counts as per-lane, and a
   // per-lane buffer resource costs a loop around every load)
   w = __builtin_amdgcn_readfirstlane(w);
-  if (w >= W) return;
-  const int64_t x0 = sk_wave_start(S.T, w, W), x1 = sk_wave_start(S.T, w + 1, W);
+  int64_t x0, x1;
+  if (p.sk_units && sk_units_even(p, S)) {
+    // one wave per unit: wave w = kvh * B + b streams all of unit (b, kvh)
+    // (the KV-head-major unit order); an empty unit gets zeros
+    if (w >= p.sk_waves) return;
+    const int kvh = w / p.B, b = w - kvh * p.B;
+    int pre, n;
+    sk_seq_of(S, b, &pre, &n);
+    if (n == 0) {
+      zero_unit(p, b, kvh);
+      return;
+    }
+    x0 = sk_unit_start(S, kvh, pre);
+    x1 = x0 + n;
+  } else {
+    if (w >= W) return;
+    x0 = sk_wave_start(S.T, w, W);
+    x1 = sk_wave_start(S.T, w + 1, W);
+  }
   if (FUSED) zero_empty_units(p, S, w, W);
   Unit<KT, D> U;
   Acc<D> A;

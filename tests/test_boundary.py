@@ -134,6 +134,28 @@ def test_plan_stream_k():
     assert plan(batch=257, **lat)["split_pages"] > 0
 
 
+def test_plan_one_wave_per_windowed_unit():
+    # with a window, the merge chosen by default and no forced wave count, a
+    # batch of at least two units per CU gets B * Hkv waves (the kernels run
+    # one per unit when the units are even) with workspace for equal shares
+    # over them, and head-grouped workgroups of up to units / CUs waves
+    fp8 = dict(batch=128, num_q_heads=64, num_kv_heads=8, kv_dtype=torch.float8_e4m3fn)
+    p = plan(window=4096, **fp8)
+    assert p["ctas_per_split_grid"] == 1024 and p["waves_per_workgroup"] == 4
+    assert p["single_launch"] == 0
+    assert p["workspace_bytes"] >= 2 * 1024 * 8 * (128 * 4 + 8)
+    assert plan(window=0, **fp8)["ctas_per_split_grid"] == 2048           # no window
+    assert plan(window=4096, **dict(fp8, batch=63))["ctas_per_split_grid"] == 2048  # 504 units
+    assert plan(window=4096, **dict(fp8, batch=64))["ctas_per_split_grid"] == 512
+    assert plan(window=4096, **dict(fp8, batch=64))["waves_per_workgroup"] == 2
+    assert plan(window=4096, target_ctas=300, **fp8)["ctas_per_split_grid"] == 300
+    assert plan(window=4096, single_launch=True, **fp8)["ctas_per_split_grid"] == 2048
+    assert plan(window=4096, batch=512, num_q_heads=32, num_kv_heads=8)["waves_per_workgroup"] == 8
+    assert plan(window=4096, batch=300, num_q_heads=6, num_kv_heads=6)["waves_per_workgroup"] == 6
+    lat = dict(batch=256, num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512)
+    assert plan(window=4096, **lat)["ctas_per_split_grid"] == 256          # latent: its own plan
+
+
 def test_plan_stream_k_tile_count_edge():
     # the stream-K kernels count tiles (16 tokens; 32 for the latent cache)
     # in 32-bit integers: the last problem under 2^31 tiles keeps stream-K,

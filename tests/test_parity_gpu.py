@@ -870,3 +870,54 @@ def test_fp8_output_needs_an_fp8_cache():
         pkv.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"],
                         inp["seq_lens"], out, num_kv_heads=w.num_kv_heads, page_size=w.page_size,
                         kv_layout=w.kv_layout)
+
+
+def _units_even(w, lens):
+    """Which schedule the one-wave-per-unit plan runs: with 16-token tiles of
+    the visible span [max(0, L - Tq + 1 - window), L), one wave per unit
+    when 4 * max(tiles) * B <= 5 * sum(tiles), equal shares otherwise."""
+    n = []
+    for L in lens:
+        lo = max(0, L - w.q_seq_len + 1 - w.window)
+        n.append((L + 15) // 16 - lo // 16 if L > lo else 0)
+    return 4 * max(n) * len(lens) <= 5 * sum(n)
+
+
+@pytest.mark.parametrize("kv, hkv, cus, lens, even", [
+    ("fp8", 2, 4, [600, 1600, 900, 1300, 700], True),
+    ("fp8", 8, 2, [0, 700, 800, 900, 1000, 1100, 1200, 1300, 1400, 1500], True),
+    ("fp8", 4, 2, [250, 300, 301, 1000, 1200], True),
+    ("fp8", 8, 2, [0, 1, 299, 300, 301, 2000, 0, 17], False),
+    ("fp8", 6, 1, [5, 700, 0, 1200, 64], False),
+    ("bf16", 8, 4, [1000, 1500, 400, 333, 1200], True),
+    ("bf16", 1, 2, [0, 0, 33, 900, 4000], False),
+    ("spec", 4, 2, [290, 3000, 1200, 301], True),
+    ("spec", 4, 2, [0, 3, 4, 300, 1200, 301], False),
+])
+def test_stream_k_one_wave_per_windowed_unit(kv, hkv, cus, lens, even):
+    # with a window and at least two units per CU the plan launches one wave
+    # per (sequence, KV head) unit; the kernels give each unit its own wave
+    # when the units are even (here: empty units, units shorter than the
+    # window and units cut by it) and equal shares otherwise
+    base = {"fp8": SMALL["fp8"], "bf16": SMALL["gqa"].replace(window=300),
+            "spec": SMALL["spec"].replace(window=280)}[kv]
+    w = base.replace(num_kv_heads=hkv, num_q_heads=(base.num_q_heads // base.num_kv_heads) * hkv,
+                     batch=len(lens), seq_len_range=(1, 4000))
+    assert _units_even(w, lens) == even
+    inp = make(w, seed=90 + hkv, seq_lens=lens)
+    p = pkv.query_plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=hkv,
+                       head_dim_qk=w.head_dim_qk, head_dim_v=w.head_dim_v,
+                       pages_per_seq=inp["page_table"].shape[1], page_size=w.page_size,
+                       q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, window=w.window,
+                       q_seq_len=w.q_seq_len, num_cus=cus)
+    print(f"[case] unit waves {kv} Hkv={hkv} cus={cus} lens={lens} even={even}: {p}", flush=True)
+    assert p["ctas_per_split_grid"] == w.batch * hkv and p["single_launch"] == 0
+    ref = run_oracle(w, inp)
+    got = run_gpu(w, inp, num_cus=cus)
+    assert_parity(w, got, ref, f"unit/{kv}/Hkv{hkv}/even{even}")
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert torch.equal(got[b].float().cpu(), torch.zeros_like(got[b].float().cpu()))
+    # the same call planned as equal shares (forced wave count) agrees
+    other = run_gpu(w, inp, target_ctas=7)
+    assert_parity(w, other, ref, f"unit-vs-shares/{kv}/Hkv{hkv}")
