@@ -60,6 +60,29 @@ __device__ __forceinline__ void lds_sync() {
 // reads (16 rows, 32 bytes) spread over the banks.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ (r & 7); }
 
+// Maxima of finite-or-minus-infinity scores.  The IEEE-mode lowering of
+// fmaxf quiets each operand with an extra v_max_f32 x, x first; these take
+// one instruction per two or three operands.
+__device__ __forceinline__ float vmax2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// The maximum over the four 16-lane row groups (lanes n, n + 16, n + 32,
+// n + 48 hold the same query row).
+__device__ __forceinline__ float row_max4(float x) {
+  float2 a = row_partner16(x);
+  x = vmax2(a.x, a.y);
+  a = row_partner32(x);
+  return vmax2(a.x, a.y);
+}
+
 // Online-softmax state of one 16-query sub-block: the reference max (log2
 // units), the O^T accumulators, and lsum = P . ones, i.e. every element of
 // lsum holds the lane's row sum of the rounded probabilities (the matrix
@@ -230,19 +253,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       uint4 pw[kSub];
 #pragma unroll
       for (int b = 0; b < kSub; ++b) {
-        const bool edge = key0 + 32 > lim_lo[b];
-        // raw scores, masked; the scale (> 0) enters once, in the exponent
+        // raw scores; the scale (> 0) enters once, in the exponent.  Only
+        // a tile that reaches past some row's last key (wave-uniform test)
+        // needs the causal mask.
         float x[8];
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = key0 + 16 * kb2 + 4 * g + i;
-            x[4 * kb2 + i] = (!edge || key < lim[b]) ? sc[b][kb2][i] : kNegInfR;
-          }
-        float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        tmax = max_across_rows(tmax) * p.scale_log2;
+          for (int i = 0; i < 4; ++i) x[4 * kb2 + i] = sc[b][kb2][i];
+        if (key0 + 32 > lim_lo[b]) {
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (key0 + 16 * kb2 + 4 * g + i >= lim[b]) x[4 * kb2 + i] = kNegInfR;
+        }
+        float tmax = vmax3(vmax3(x[0], x[1], x[2]), vmax3(x[3], x[4], x[5]), vmax2(x[6], x[7]));
+        tmax = row_max4(tmax) * p.scale_log2;
         const bool bump = tmax > A[b].m + kSlack;
         const float m_new = bump ? tmax : A[b].m;
         const float m_ref = m_new == kNegInfR ? 0.f : m_new;
