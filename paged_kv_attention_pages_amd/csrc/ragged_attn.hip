@@ -169,9 +169,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int k_tok = p.Hkv * DQK * 2, v_tok = p.Hkv * DV * 2;   // bytes per key row
   const uint8_t* kb = (const uint8_t*)p.k + (int64_t)k0 * k_tok + (int64_t)kvh * DQK * 2;
   const uint8_t* vb = (const uint8_t*)p.v + (int64_t)k0 * v_tok + (int64_t)kvh * DV * 2;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kb, (uint32_t)((int64_t)(p.total_k - k0) * k_tok - kvh * DQK * 2));
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vb, (uint32_t)((int64_t)(p.total_k - k0) * v_tok - kvh * DV * 2));
-  const __amdgpu_buffer_rsrc_t rz = make_rsrc(kb, 0u);
+  const uint32_t k_bytes = (uint32_t)((int64_t)(p.total_k - k0) * k_tok - kvh * DQK * 2);
+  const uint32_t v_bytes = (uint32_t)((int64_t)(p.total_k - k0) * v_tok - kvh * DV * 2);
   // this thread's chunks of a tile: i < KI are K chunks, the rest V chunks
   int crow[NCH], cvoff[NCH], clds[NCH];
 #pragma unroll
@@ -196,27 +195,50 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int so = live ? t * TK * (i < KI ? k_tok : v_tok) : 0;
-      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(live ? (i < KI ? rk : rv) : rz, cvoff[i], so, 0);
+      // past the last tile the resource has size zero: the load returns
+      // zeros and the wait counts stay the same on every step (the size is
+      // a scalar select, so the resource stays in scalar registers)
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(i < KI ? kb : vb, live ? (i < KI ? k_bytes : v_bytes) : 0u);
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, cvoff[i], so, 0);
       stg[i] = make_uint4(a[0], a[1], a[2], a[3]);
     }
   };
   // keys past the last one the workgroup's rows see are stored as zeros, so
-  // a zero weight never meets a non-finite value
-  auto lwrite = [&](int t) {
-    uint8_t* base = lds + (t & 1) * STAGE;
+  // a zero weight never meets a non-finite value (only the last tile has
+  // such keys: the test is wave-uniform)
+  auto lwrite = [&](auto stage_c, int t) {
+    constexpr int SG = decltype(stage_c)::value;
+    uint8_t* base = lds + SG * STAGE;
+    if (t * TK + TK <= kend) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const bool keep = t * TK + crow[i] < kend;
-      *(uint4*)(base + clds[i]) = keep ? stg[i] : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < NCH; ++i) *(uint4*)(base + clds[i]) = stg[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const bool keep = t * TK + crow[i] < kend;
+        *(uint4*)(base + clds[i]) = keep ? stg[i] : make_uint4(0, 0, 0, 0);
+      }
     }
   };
-  // per-lane LDS offsets of the operand reads
-  int koff[KSTEPS];
-#pragma unroll
-  for (int st = 0; st < KSTEPS; ++st) koff[st] = n * KROW + 16 * swz(n, 4 * st + g);
+  // Per-lane LDS offsets of the operand reads, split so that everything
+  // that varies with the step, the key block or the stage is an immediate.
+  // K fragment of step st: row n, chunk (4 st + g) ^ (n mod 8) = 4 (st ^ b)
+  // + (g ^ (n mod 4)) with b = bit 2 of n; st ^ b is st + b for even st and
+  // st - b for odd st.
+  const int kb_bit = (n >> 2) & 1;
+  const int kofs_e = n * KROW + 16 * (g ^ (n & 3)) + 64 * kb_bit;
+  const int kofs_o = kofs_e - 128 * kb_bit;
   // transposed V read of dims 16 jd .. + 15: lane (a + 4 jj) of its group
-  // addresses key 4 g + jj (+ 16 for the second block), dims 16 jd + 4 a .. + 3
+  // addresses key r0 = 4 g + jj (r0 + 16 for the second block, the same
+  // swizzle), dims 16 jd + 4 a .. + 3, i.e. chunk c = 2 jd + a / 2 at
+  // c ^ m, m = r0 mod 8; with mm = m / 2 that is 2 ((jd & ~3) + ((jd & 3) ^
+  // mm)) + (a / 2 ^ m mod 2): one base per value of jd mod 4.
   const int va = n & 3, vjj = n >> 2;
+  const int vr0 = 4 * g + vjj, vm = vr0 & 7;
+  int vofs[4];
+#pragma unroll
+  for (int qd = 0; qd < 4; ++qd)
+    vofs[qd] = KBYTES + vr0 * VROW + 32 * (qd ^ (vm >> 1)) + 16 * ((va >> 1) ^ (vm & 1)) + 8 * (va & 1);
   RAcc<DV> A[kSub];
 #pragma unroll
   for (int b = 0; b < kSub; ++b) {
@@ -225,15 +247,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int jd = 0; jd < DT; ++jd) A[b].o[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  using Stage0 = std::integral_constant<int, 0>;
+  using Stage1 = std::integral_constant<int, 1>;
   gload(0);
-  lwrite(0);
+  lwrite(Stage0{}, 0);
   gload(1);
   lds_sync();
-  for (int t = 0; t < nt; ++t) {
+  // one tile; its LDS stage SG = t mod 2 is a compile-time constant, so
+  // every operand read is a per-lane base plus an immediate offset
+  auto tile = [&](auto stage_c, int t) {
+    constexpr int SG = decltype(stage_c)::value;
 #pragma unroll
     for (int hf = 0; hf < TK / 32; ++hf) {
-    const uint8_t* kt = lds + (t & 1) * STAGE + hf * 32 * KROW;
-    const uint8_t* vt = lds + (t & 1) * STAGE + KBYTES + hf * 32 * VROW;
+    const uint8_t* kt = lds + SG * STAGE + hf * 32 * KROW;
+    const uint8_t* vt = lds + SG * STAGE + hf * 32 * VROW;
     const int key0 = t * TK + 32 * hf;
     if (has_rows && key0 < kend_w) {
       // ---- S^T of both 16-key blocks for both sub-blocks
@@ -244,7 +271,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       for (int st = 0; st < KSTEPS; ++st)
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
-          const uint4 kf = *(const uint4*)(kt + kb2 * 16 * KROW + koff[st]);
+          const uint4 kf = *(const uint4*)(kt + kb2 * 16 * KROW + 64 * st + ((st & 1) ? kofs_o : kofs_e));
 #pragma unroll
           for (int b = 0; b < kSub; ++b) sc[b][kb2] = mfma_k32<QT>(kf, qb[b][st], sc[b][kb2]);
         }
@@ -289,10 +316,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       // ---- O^T += V^T . P^T, 16 dims at a time
 #pragma unroll
       for (int jd = 0; jd < DT; ++jd) {
-        const int c = 2 * jd + (va >> 1), bo = 8 * (va & 1);
-        const int r0 = 4 * g + vjj, r1 = r0 + 16;
-        const uint2 v0 = lds_tr16(vt + r0 * VROW + 16 * swz(r0, c) + bo);
-        const uint2 v1 = lds_tr16(vt + r1 * VROW + 16 * swz(r1, c) + bo);
+        const uint8_t* va0 = vt + vofs[jd & 3] + 32 * (jd & ~3);
+        const uint2 v0 = lds_tr16(va0);
+        const uint2 v1 = lds_tr16(va0 + 16 * VROW);
         const uint4 vop = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
         for (int b = 0; b < kSub; ++b) A[b].o[jd] = mfma_k32<QT>(vop, pw[b], A[b].o[jd]);
@@ -306,9 +332,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
     // the next tile into the stage tile t - 1 used (every wave finished it
     // before the last barrier), then the loads of the one after
-    if (t + 1 < nt) lwrite(t + 1);
+    if (t + 1 < nt) lwrite(std::integral_constant<int, 1 - SG>{}, t + 1);
     gload(t + 2);
     lds_sync();
+  };
+  for (int t = 0; t < nt; t += 2) {
+    tile(Stage0{}, t);
+    if (t + 1 < nt) tile(Stage1{}, t + 1);
   }
 #pragma unroll
   for (int b = 0; b < kSub; ++b) {
