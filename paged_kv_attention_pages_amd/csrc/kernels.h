@@ -74,7 +74,7 @@ struct RaggedParams {
   float* lse;                 // element (n, h) at n * lse_sn + h * lse_sh, or null
   int64_t lse_sn, lse_sh;
   int num_seqs, Hq, Hkv, G, Dqk, Dv, total_q, total_k, max_q_len, causal;
-  int q_blocks;               // workgroups per (sequence, head) (set by the launcher)
+  int q_blocks;               // query blocks per (sequence, head) (set by the launcher)
   float scale_log2;           // sm_scale * log2(e)
 };
 hipError_t launch_ragged_attn(int dtype, const RaggedParams& p, hipStream_t s);

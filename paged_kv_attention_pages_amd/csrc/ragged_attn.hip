@@ -96,10 +96,10 @@ struct RAcc {
 
 }  // namespace
 
-// One workgroup of NW waves per 32 NW queries of a (sequence, head): the
-// workgroup loads each 8 NW-key tile of K and V once (16-byte loads spread over
-// its 256 threads, straight into registers, then into a two-stage LDS ring),
-// and every wave reads its matrix operands from LDS.  Wave w holds queries
+// One query block (32 NW queries of a (sequence, head)) on a workgroup of
+// NW waves: the workgroup loads each 8 NW-key tile of K and V once (16-byte
+// loads spread over its threads, straight into registers, then into a
+// two-stage LDS ring), and every wave reads its matrix operands from LDS.  Wave w holds queries
 // 32 w .. 32 w + 31 as two 16-query sub-blocks.  Per tile and sub-block:
 //   S^T (2 x 16 keys x 16 queries) = K . Q^T   -- 16x16x32 MFMAs from LDS
 //   online softmax of the 32 keys per lane
@@ -108,8 +108,11 @@ struct RAcc {
 // The MFMA contraction index 8 g + c of P.V stands for key 4 g + c of the
 // first 16-key block (c < 4) or 16 + 4 g + c - 4 of the second: the order in
 // which the lane holds its scores, and the order of the two transposed reads.
+template <int DQK, int DV, int NW>
+constexpr int ragged_stage_bytes() { return 8 * NW * (DQK + DV) * 2; }
+
 template <int QT, int DQK, int DV, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void ragged_attn_kernel(RaggedParams p) {
+__device__ __forceinline__ void ragged_item(const RaggedParams& p, uint8_t* lds, int pair, int qblk) {
   constexpr int kThreadsWg = 64 * NW, kQueriesPerWg = NW * kQueriesPerWave;
   constexpr int KSTEPS = DQK / 32, DT = DV / 16;
   constexpr int KC = DQK / 8, VC = DV / 8;              // 16-byte chunks per row
@@ -118,18 +121,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   constexpr int KBYTES = TK * KROW, STAGE = KBYTES + TK * VROW;
   constexpr int KI = TK * KC / kThreadsWg, NCH = TK * (KC + VC) / kThreadsWg;  // chunks per thread
   static_assert(TK * KC % kThreadsWg == 0 && TK * VC % kThreadsWg == 0, "whole K and V loads per thread");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * STAGE];
+  static_assert(STAGE == ragged_stage_bytes<DQK, DV, NW>(), "stage size");
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
-  // workgroups are dealt to the 8 XCDs round robin (id mod 8); every query
-  // block of one (sequence, head) pair gets an id of the same residue, so
-  // they share one XCD's L2 and its copy of the pair's K/V rows: XCD x takes
-  // pairs x, x + 8, ..., each pair's blocks from the last (causal: the most
-  // keys) to the first, so the cheap blocks fill the tail
-  const int wg = blockIdx.x, xcd = wg & 7, j = wg >> 3;
-  const int pair = 8 * (j / p.q_blocks) + xcd;
-  const int qblk = p.q_blocks - 1 - (j - (j / p.q_blocks) * p.q_blocks);
-  if (pair >= p.num_seqs * p.Hq) return;
   const int s = pair / p.Hq, h = pair - s * p.Hq, kvh = h / p.G;
   // sequence bounds, clamped to the tensors so that any cu_seqlens stay in bounds
   const int q0 = min(max(p.cu_q[s], 0), p.total_q), q1 = min(max(p.cu_q[s + 1], q0), p.total_q);
@@ -359,6 +353,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
+// Workgroups are dealt to the 8 XCDs round robin (id mod 8); every query
+// block of one (sequence, head) pair gets an id of the same residue, so they
+// share one XCD's L2 and its copy of the pair's K/V rows: XCD x takes pairs
+// x, x + 8, ... in order.  Causal blocks differ in cost (block j sees j + 1
+// blocks of keys), so a causal workgroup takes two blocks of its pair, j from
+// the end and j from the start, one after the other: every workgroup then has
+// the same work, and a pair takes half as many workgroups.  Other calls take
+// one block per workgroup, the pair's blocks side by side (they read the
+// same K/V rows at about the same time).
+template <int QT, int DQK, int DV, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void ragged_attn_kernel(RaggedParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * ragged_stage_bytes<DQK, DV, NW>()];
+  const int xcd = blockIdx.x & 7, jw = blockIdx.x >> 3;
+  const int per_pair = p.causal ? (p.q_blocks + 1) / 2 : p.q_blocks;
+  const int pl = jw / per_pair, jj = jw - pl * per_pair;
+  const int pair = 8 * pl + xcd;
+  if (pair >= p.num_seqs * p.Hq) return;
+  ragged_item<QT, DQK, DV, NW>(p, lds, pair, p.q_blocks - 1 - jj);
+  if (p.causal && jj != p.q_blocks - 1 - jj) ragged_item<QT, DQK, DV, NW>(p, lds, pair, jj);
+}
+
 // Causal calls run four-wave workgroups (128 queries, 32-key tiles): the
 // rows of a workgroup see different key counts and wait for each other at
 // every tile, so smaller groups idle less.  Other calls run eight waves (256
@@ -368,9 +383,12 @@ static hipError_t launch_ragged(const RaggedParams& p, hipStream_t s) {
   const int nw = p.causal ? 4 : 8;
   RaggedParams q = p;
   q.q_blocks = (p.max_q_len + 32 * nw - 1) / (32 * nw);
-  const int64_t groups = ((int64_t)p.num_seqs * p.Hq + 7) / 8;
-  const int64_t n = 8 * groups * q.q_blocks;
+  // workgroups: pairs per XCD (rounded up) x workgroups per pair, per XCD
+  const int64_t per_xcd = ((int64_t)p.num_seqs * p.Hq + 7) / 8;
+  const int64_t per_pair = p.causal ? (q.q_blocks + 1) / 2 : q.q_blocks;
+  const int64_t n = 8 * per_xcd * per_pair;
   if (n >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (n == 0) return hipSuccess;
   if (nw == 4)
     hipLaunchKernelGGL((ragged_attn_kernel<QT, DQK, DV, 4>), dim3((unsigned)n), dim3(256), 0, s, q);
   else

@@ -79,6 +79,15 @@ def test_ragged_head_groupings(Hq, Hkv):
     _check(out, lse, ref, ref_lse, torch.bfloat16, f"Hq={Hq} Hkv={Hkv}")
 
 
+@pytest.mark.parametrize("lens", [[300], [300, 260, 129, 385], [640, 1, 129], [0, 511, 128]])
+def test_ragged_causal_block_pairs(lens):
+    # a causal workgroup takes query blocks j and last - j of one pair: odd
+    # and even block counts (3, 4, 5 and 4 blocks of 128 queries), sequences
+    # shorter than max_q_len (their later blocks have no rows) and empty ones
+    out, lse, ref, ref_lse = _run(lens, lens, 8, 2, 192, 128, torch.bfloat16, True, seed=8)
+    _check(out, lse, ref, ref_lse, torch.bfloat16, f"pairs {lens}")
+
+
 def test_ragged_long_sequence_and_scale():
     # 1000 queries over 1500 keys (16 query blocks of 64, 94 key tiles); a
     # larger softmax scale sharpens the weights
