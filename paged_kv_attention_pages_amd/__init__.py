@@ -391,7 +391,7 @@ def decode_attn_noalloc(q, k_cache, v_cache, page_table, seq_lens, output, *, nu
                         page_size, sinks=None, q_scale=1.0, kv_scale=1.0, sliding_win_size=0,
                         kv_layout="NHD", q_seq_len=1, mask=None, head_dim_v=None, path=None,
                         split_pages=0, target_ctas=0, stream=None, split_event=None,
-                        single_launch=None, rcp_out_scale=1.0):
+                        single_launch=None, rcp_out_scale=1.0, num_cus=0):
     """``decode_attn`` without a workspace and without allocating anything.
 
     The partial results live in the library's static per-GPU scratch
@@ -405,7 +405,7 @@ def decode_attn_noalloc(q, k_cache, v_cache, page_table, seq_lens, output, *, nu
     opts, d, q_scale, kv_scale = _decode_prep(
         q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size, sinks,
         q_scale, kv_scale, kv_layout, q_seq_len, mask, head_dim_v, path, split_pages,
-        target_ctas, split_event, single_launch, rcp_out_scale)
+        target_ctas, split_event, single_launch, rcp_out_scale, num_cus)
     dev = q.get_device()
     if stream is None:
         stream = _current_stream(dev)

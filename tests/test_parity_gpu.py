@@ -725,18 +725,20 @@ def test_stream_k_wide_batches(kind, B):
         assert torch.equal(got[L == 0].float().cpu(), torch.zeros_like(got[L == 0].float().cpu()))
 
 
-@pytest.mark.parametrize("name", ["gqa", "spec", "mla"])
+@pytest.mark.parametrize("name", ["gqa", "spec", "mla", "fp8_unit_waves"])
 def test_graph_replay_matches_eager(name):
     # a captured call (workspace passed in, so nothing is allocated inside the
-    # capture) replayed several times, with eager work between the replays
-    w = SMALL[name] if name != "mla" else MLA_SMALL
+    # capture) replayed several times, with eager work between the replays;
+    # fp8_unit_waves: a window and two units per CU (one wave per unit)
+    kw = dict(num_cus=2) if name == "fp8_unit_waves" else {}
+    w = MLA_SMALL if name == "mla" else SMALL[name.split("_")[0]]
     print(f"[case] graph replay {name}", flush=True)
     inp = make(w, seed=99)
     plan = pkv.query_plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                           head_dim_qk=w.head_dim_qk, head_dim_v=w.head_dim_v,
                           pages_per_seq=inp["page_table"].shape[1], page_size=w.page_size,
                           q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, window=w.window,
-                          q_seq_len=w.q_seq_len)
+                          q_seq_len=w.q_seq_len, **kw)
     ws = torch.empty(max(plan["workspace_bytes"], 256), dtype=torch.uint8, device=DEV)
     out = torch.full((w.batch, w.q_seq_len, w.num_q_heads, w.head_dim_v), float("nan"),
                      dtype=w.q_dtype, device=DEV)
@@ -746,7 +748,7 @@ def test_graph_replay_matches_eager(name):
                         inp["seq_lens"], out, ws, num_kv_heads=w.num_kv_heads,
                         page_size=w.page_size, sinks=inp["sinks"], q_scale=w.q_scale,
                         kv_scale=w.kv_scale, sliding_win_size=w.window, kv_layout=w.kv_layout,
-                        q_seq_len=w.q_seq_len, mask=inp["mask"], head_dim_v=w.head_dim_v)
+                        q_seq_len=w.q_seq_len, mask=inp["mask"], head_dim_v=w.head_dim_v, **kw)
 
     call()
     torch.cuda.synchronize()

@@ -65,6 +65,8 @@ CASES = {
     "mla": dict(),
     "gqa_single_launch": dict(single_launch=True, target_ctas=7),
     "gqa_split_grid": dict(split_pages=2),
+    # a window and two units per CU: one wave per (sequence, KV head)
+    "fp8_unit_waves": dict(num_cus=2),
 }
 
 
