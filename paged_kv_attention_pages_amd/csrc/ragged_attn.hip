@@ -100,8 +100,9 @@ struct RAcc {
 // One query block (32 NW queries of a (sequence, head)) on a workgroup of
 // NW waves: the workgroup loads each 8 NW-key tile of K and V once (16-byte
 // loads spread over its threads, straight into registers, then into a
-// two-stage LDS ring), and every wave reads its matrix operands from LDS.  Wave w holds queries
-// 32 w .. 32 w + 31 as two 16-query sub-blocks.  Per tile and sub-block:
+// two-stage LDS ring), and every wave reads its matrix operands from LDS.
+// Wave w holds queries 32 w .. 32 w + 31 as two 16-query sub-blocks.  Per
+// tile, 32 keys at a time, and sub-block:
 //   S^T (2 x 16 keys x 16 queries) = K . Q^T   -- 16x16x32 MFMAs from LDS
 //   online softmax of the 32 keys per lane
 //   O^T (Dv x 16 queries) += V^T . P^T          -- 16x16x32 MFMAs, V^T by
