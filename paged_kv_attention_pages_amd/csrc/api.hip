@@ -286,9 +286,10 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
     // equal shares over them; the kernels choose between the two on the
     // device, from the lengths (sk_units_even), so a batch of mostly short
     // sequences still gets equal shares.  Used by default when the units give
-    // every CU at least two waves.
+    // every CU two to eight waves (more would only grow the equal-shares
+    // workspace, two partial slots per unit).
     if (path == PKV_PATH_MFMA && window > 0 && mode == 0 && !(opts && opts->target_ctas > 0) &&
-        units >= 2 * (int64_t)cus && units <= (1 << 20)) {
+        units >= 2 * (int64_t)cus && units <= 8 * (int64_t)cus) {
       pl->unit_aligned = true;
       pl->sk_waves = (int)units;
       pl->sk_hb = 1;

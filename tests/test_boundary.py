@@ -150,8 +150,11 @@ def test_plan_one_wave_per_windowed_unit():
     assert plan(window=4096, **dict(fp8, batch=64))["waves_per_workgroup"] == 2
     assert plan(window=4096, target_ctas=300, **fp8)["ctas_per_split_grid"] == 300
     assert plan(window=4096, single_launch=True, **fp8)["ctas_per_split_grid"] == 2048
-    assert plan(window=4096, batch=512, num_q_heads=32, num_kv_heads=8)["waves_per_workgroup"] == 8
+    assert plan(window=4096, batch=256, num_q_heads=32, num_kv_heads=8)["waves_per_workgroup"] == 8
     assert plan(window=4096, batch=300, num_q_heads=6, num_kv_heads=6)["waves_per_workgroup"] == 6
+    # up to eight units per CU; beyond, equal shares over the usual waves
+    assert plan(window=4096, batch=256, num_q_heads=32, num_kv_heads=8)["ctas_per_split_grid"] == 2048
+    assert plan(window=4096, batch=257, num_q_heads=32, num_kv_heads=8)["ctas_per_split_grid"] == 1024
     lat = dict(batch=256, num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512)
     assert plan(window=4096, **lat)["ctas_per_split_grid"] == 256          # latent: its own plan
 

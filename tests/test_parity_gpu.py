@@ -887,17 +887,17 @@ def _units_even(w, lens):
 
 @pytest.mark.parametrize("kv, hkv, cus, lens, even", [
     ("fp8", 2, 4, [600, 1600, 900, 1300, 700], True),
-    ("fp8", 8, 2, [0, 700, 800, 900, 1000, 1100, 1200, 1300, 1400, 1500], True),
-    ("fp8", 4, 2, [250, 300, 301, 1000, 1200], True),
-    ("fp8", 8, 2, [0, 1, 299, 300, 301, 2000, 0, 17], False),
-    ("fp8", 6, 1, [5, 700, 0, 1200, 64], False),
-    ("bf16", 8, 4, [1000, 1500, 400, 333, 1200], True),
+    ("fp8", 8, 16, [0, 700, 800, 900, 1000, 1100, 1200, 1300, 1400, 1500], True),
+    ("fp8", 4, 4, [250, 300, 301, 1000, 1200], True),
+    ("fp8", 8, 16, [0, 1, 299, 300, 301, 2000, 0, 17], False),
+    ("fp8", 6, 8, [5, 700, 0, 1200, 64], False),
+    ("bf16", 8, 8, [1000, 1500, 400, 333, 1200], True),
     ("bf16", 1, 2, [0, 0, 33, 900, 4000], False),
     ("spec", 4, 2, [290, 3000, 1200, 301], True),
-    ("spec", 4, 2, [0, 3, 4, 300, 1200, 301], False),
+    ("spec", 4, 4, [0, 3, 4, 300, 1200, 301], False),
 ])
 def test_stream_k_one_wave_per_windowed_unit(kv, hkv, cus, lens, even):
-    # with a window and at least two units per CU the plan launches one wave
+    # with a window and two to eight units per CU the plan launches one wave
     # per (sequence, KV head) unit; the kernels give each unit its own wave
     # when the units are even (here: empty units, units shorter than the
     # window and units cut by it) and equal shares otherwise
