@@ -228,14 +228,15 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
   // Stream-K schedule (matrix-core path, batch <= 256, no forced split size):
   // persistent waves (measured best: one per SIMD for 16-bit caches, each
   // with a three-stage pipeline in flight); 2 partial slots per wave.
-  // The latent-cache kernel runs the same schedule over 32-token tiles with
-  // one four-wave workgroup per CU (its register budget allows no more).
+  // The latent-cache kernel runs the same schedule over 32-token tiles (64
+  // for an fp8 cache) with one eight-wave workgroup per CU (its LDS ring
+  // allows no more).
   // Both kernels count tiles in 32-bit integers (the tiles of one KV head
   // over all sequences, per-sequence prefixes, unit offsets), so the whole
   // tile stream must stay under 2^31 tiles; a sequence's visible tokens span
   // at most cdiv(pages_max * ps, tile) + 1 aligned tiles.  Larger problems
   // take the split grid.
-  const int64_t sk_tile = path == PKV_PATH_MFMA_MLA ? 32 : 16;
+  const int64_t sk_tile = path != PKV_PATH_MFMA_MLA ? 16 : d->kv_dtype == PKV_FP8_E4M3 ? 64 : 32;
   const bool sk_path = (path == PKV_PATH_MFMA || path == PKV_PATH_MFMA_MLA) &&
                        units * (cdiv(pages_max * ps, sk_tile) + 1) < ((int64_t)1 << 31);
   // (up to 256 sequences; the matrix-core kernel with head dims up to 128
@@ -261,9 +262,9 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
         }
     pl->split_pages = 0;
     pl->max_splits = 0;
-    // the latent kernel for 16-bit caches keeps 64 padded rows per slot, its
-    // partial outputs in the P.V waves' register order (see combine.hip)
-    pl->lat_ws = path == PKV_PATH_MFMA_MLA && d->kv_dtype != PKV_FP8_E4M3;
+    // the latent kernel keeps 64 padded rows per slot, its partial outputs
+    // in the P.V waves' register order (see combine.hip)
+    pl->lat_ws = path == PKV_PATH_MFMA_MLA;
     const size_t nrow = (size_t)2 * pl->sk_waves * (pl->lat_ws ? 64 : R);
     pl->ws_o_bytes = nrow * Dv * sizeof(float);
     pl->ws_ml_off = (pl->ws_o_bytes + 255) & ~(size_t)255;
@@ -401,7 +402,7 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
   p.max_splits = pl.max_splits;
   p.sk_waves = pl.sk_waves;
   p.sk_hb = pl.sk_hb;
-  p.sk_shift = pl.path == PKV_PATH_MFMA_MLA ? 5 : 4;
+  p.sk_shift = pl.path != PKV_PATH_MFMA_MLA ? 4 : d->kv_dtype == PKV_FP8_E4M3 && pl.lat_ws ? 6 : 5;
   p.qk_scale_log2 = (float)((double)q_scale * (double)kv_scale / std::sqrt((double)Dk) *
                             1.4426950408889634);
   p.out_scale = kv_scale;
@@ -425,9 +426,9 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
   switch (pl.path) {
     case PKV_PATH_VALU: e = pkv::launch_split_valu(d->q_dtype, d->kv_dtype, (int)Dk, p, s); break;
     case PKV_PATH_MFMA_MLA:
-      // 16-bit caches on the stream-K schedule: the wave-specialised kernel;
-      // fp8 caches and the split grid: the kernel that stages tiles in registers
-      e = pl.lat_ws ? pkv::launch_split_mla_ws(d->q_dtype, p, s)
+      // the stream-K schedule: the wave-specialised kernel; the split grid:
+      // the kernel that stages tiles in registers
+      e = pl.lat_ws ? pkv::launch_split_mla_ws(d->q_dtype, d->kv_dtype, p, s)
               : pkv::launch_split_mla(d->q_dtype, d->kv_dtype, p, s);
       break;
     default: e = pkv::launch_split_mfma16(d->q_dtype, d->kv_dtype, (int)Dk, p, s); break;

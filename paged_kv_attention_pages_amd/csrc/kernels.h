@@ -15,9 +15,9 @@ hipError_t launch_split_mfma16(int q_dtype, int kv_dtype, int D, const Params& p
 // rows whose leading 512 entries are V.
 hipError_t launch_split_mla(int q_dtype, int kv_dtype, const Params& p, hipStream_t s);
 
-// The same over a 16-bit latent cache on the stream-K schedule, with score
-// and P.V work on separate waves and the tiles loaded straight into LDS.
-hipError_t launch_split_mla_ws(int q_dtype, const Params& p, hipStream_t s);
+// The same on the stream-K schedule, with score and P.V work on separate
+// waves and the tiles loaded straight into LDS (16-bit or fp8 caches).
+hipError_t launch_split_mla_ws(int q_dtype, int kv_dtype, const Params& p, hipStream_t s);
 
 // Split-KV decode on the vector ALUs, up to 8 rows per KV head.
 hipError_t launch_split_valu(int q_dtype, int kv_dtype, int D, const Params& p, hipStream_t s);
