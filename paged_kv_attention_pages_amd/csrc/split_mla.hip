@@ -25,9 +25,9 @@
 // gfx950, so reads carry the operand traffic.  The 64 accumulator
 // registers per lane keep the working set in the 256 VGPRs of a
 // two-waves-per-SIMD budget.
-// The workgroup runs stream-K over 32-token tiles of all (sequence, KV head)
-// units (one workgroup per CU), or one (sequence, split) per workgroup under
-// the grid schedule.
+// This kernel serves the grid schedule, one (sequence, split) per workgroup
+// (batches above the stream-K limit, or a forced split size); the stream-K
+// schedule runs the wave-specialised kernel of split_mla_ws.hip.
 #include "pkv_device.h"
 #include "kernels.h"
 
@@ -519,81 +519,11 @@ __global__ __launch_bounds__(kThreads) void split_mla_kernel(Params p) {
                    (((int64_t)b * p.Hkv + kvh) * p.max_splits + split) * p.R);
 }
 
-// Stream-K schedule over 32-token tiles: workgroup w of W takes an equal
-// share of the tile stream of all units; units wholly inside its share are
-// finished here, the first and the last (when cut) leave partials in
-// workspace slots 2w and 2w+1.
-template <int QT, bool KV8, bool Q8>
-__global__ __launch_bounds__(kThreads) void split_mla_sk_kernel(Params p) {
-  resolve_scales(p);
-  __shared__ Smem sm;
-  // the schedule's per-sequence tile prefix sums and counts live in LDS, so
-  // the unit loop carries no per-lane schedule state
-  __shared__ int sk_pre[kSkMaxBatch], sk_cnt[kSkMaxBatch];
-  const int lane = threadIdx.x & 63;
-  int64_t T;
-  int T1;
-  {
-    const SkSched S = sk_schedule(p);
-    T = S.T;
-    T1 = S.T1;
-    if (wave_id() == 0) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        sk_pre[lane + 64 * c] = S.pre[c];
-        sk_cnt[lane + 64 * c] = S.cnt[c];
-      }
-    }
-  }
-  lds_barrier();
-  const int wg = blockIdx.x, W = sk_waves_eff(T, gridDim.x);
-  if (wg >= W) return;
-  // the host keeps the tile stream under 2^31 tiles for this kernel
-  const int x0 = (int)sk_wave_start(T, wg, W), x1 = (int)sk_wave_start(T, wg + 1, W);
-  const LdsOff L = lds_offsets();
-  for (int x = x0; x < x1;) {
-    Piece P;
-    QRegs Q;
-    Acc A;
-    // unit holding global tile x (units KV-head-major): its KV head, then
-    // the last sequence whose first tile is <= x within that head's tiles
-    const int kvh = x / T1, xr = x - kvh * T1;
-    int b = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int bb = lane + 64 * c;
-      const bool ok = bb < p.B && sk_pre[bb] <= xr;
-      const uint64_t m = __ballot(ok);
-      if (m != 0) b = 64 * c + 63 - __builtin_clzll(m);
-    }
-    const int pre = sk_pre[b], ntiles = sk_cnt[b];
-    const int ustart = kvh * T1 + pre;
-    const int seg_end = min(x1, ustart + ntiles);
-    const SeqGeom sg = seq_geom(p, b);
-    const int tile0 = sg.lo >> kTileShift;
-    const int t_from = tile0 + (x - ustart), t_to = tile0 + (seg_end - ustart);
-    const int tok_lo = max(t_from * kTileTok, sg.lo), tok_hi = min(t_to * kTileTok, sg.L);
-    setup_piece<KV8>(p, b, kvh, tok_lo, tok_hi, P);
-    const Run R = open_run(p, P, t_from, t_to);
-    load_q<QT, Q8>(p, P, Q);
-    reset(A);
-    stream_piece<QT, KV8>(p, P, Q, L, R, t_to, sm, A);
-    const bool complete = x == ustart && seg_end == ustart + ntiles;
-    const int slot = 2 * wg + (x == x0 ? 0 : 1);
-    finish_piece<QT>(p, P, A, complete, (int64_t)slot * p.R);
-    x = seg_end;
-  }
-}
-
 template <int QT, bool KV8, bool Q8>
 hipError_t launch_split_mla(const Params& p, hipStream_t stream) {
-  if (p.sk_waves > 0) {
-    if (p.sk_shift != kTileShift || p.B > kSkMaxBatch) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((split_mla_sk_kernel<QT, KV8, Q8>), dim3(p.sk_waves), dim3(kThreads), 0, stream, p);
-  } else {
-    dim3 grid(p.max_splits, p.Hkv, p.B);
-    hipLaunchKernelGGL((split_mla_kernel<QT, KV8, Q8>), grid, dim3(kThreads), 0, stream, p);
-  }
+  if (p.sk_waves > 0) return hipErrorInvalidValue;   // stream-K: split_mla_ws.hip
+  dim3 grid(p.max_splits, p.Hkv, p.B);
+  hipLaunchKernelGGL((split_mla_kernel<QT, KV8, Q8>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

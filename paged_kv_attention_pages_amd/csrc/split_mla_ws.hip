@@ -28,14 +28,16 @@
 // One barrier per step.  For a 16-bit tile the LDS serves 144 KB of K reads,
 // 64 KB of V reads and 12 KB of probability traffic -- against about 290 KB
 // read and 52 KB written when every wave did both products for its own rows.
-// An fp8 tile holds twice the tokens at the same bytes: its K and V
-// fragments are read as bytes and converted exactly to the 16-bit operand
-// type in registers (every e4m3fn value is exact in bf16 and f16), so the
-// products are the same as on a 16-bit image of the cache.  (gfx950's fp8
-// matrix instructions were not used for the scores: measured on random
-// e4m3fn operands, v_mfma_f32_16x16x128_f8f6f4 sums its 128 products with
-// relative errors up to ~1e-4, where the 16-bit route is exact up to fp32
-// rounding.)
+// An fp8 tile holds twice the tokens at the same bytes.  Its V fragments
+// are read as bytes and converted exactly to the 16-bit operand type in
+// registers (every e4m3fn value is exact in bf16 and f16), and so are its K
+// fragments for a 16-bit query.  With an fp8 query the scores run on the
+// fp8 matrix instruction (v_mfma_f32_16x16x128_f8f6f4) on the bytes
+// themselves: measured on random e4m3fn operands it sums its 128 products
+// with relative errors up to ~1e-4 of the sum of their magnitudes (the
+// 16-bit route is exact up to fp32 rounding), far below the quantisation of
+// the fp8 inputs; on the fp8 latent workloads the outputs' errors against
+// the oracle matched those of the exact route to three digits.
 //
 // The loads that write LDS are issued through a short asm block: the
 // compiler would otherwise wait for every outstanding one before each LDS
@@ -109,6 +111,7 @@ __device__ __forceinline__ uint8_t* slot_hi8(Smem<true>& sm, int i3) {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -443,12 +446,29 @@ __device__ __forceinline__ uint4 q_step(const Params& p, int64_t e, bool ok, int
   }
 }
 
+// An fp8 query over an fp8 cache keeps its bytes: the scores then run on the
+// fp8 matrix instructions (16x16x128), and lane group g supplies bytes
+// 16 h .. + 15 of dims 128 s + 32 g .. + 32 in k[2 s + h] (s < 4), and of the
+// rope dims 512 + 32 g .. + 32 in k[8 + h] (zeros for g >= 2).
+constexpr int kQ8Regs = 10;
+
+__device__ __forceinline__ uint4 q8_part(const Params& p, int64_t e, bool ok, int k) {
+  const int g = (threadIdx.x & 63) >> 4, s = k >> 1, h = k & 1;
+  const bool live = ok && (s < 4 || g < 2);
+  return live ? *(const uint4*)((const uint8_t*)p.q + e + 128 * s + 32 * g + 16 * h) : make_uint4(0, 0, 0, 0);
+}
+
 template <int QT, bool KV8, bool Q8>
 __device__ __forceinline__ void load_q(const Params& p, const UnitPos& u, int rb, QRegs& Q) {
   bool ok;
   const int64_t e = q_lane_offset(p, u, rb, ok);
+  if constexpr (KV8 && Q8) {
 #pragma unroll
-  for (int s = 0; s < kQkSteps; ++s) Q.k[s] = q_step<QT, KV8, Q8>(p, e, ok, s);
+    for (int k = 0; k < kQ8Regs; ++k) Q.k[k] = q8_part(p, e, ok, k);
+  } else {
+#pragma unroll
+    for (int s = 0; s < kQkSteps; ++s) Q.k[s] = q_step<QT, KV8, Q8>(p, e, ok, s);
+  }
 }
 
 // The next unit's query slice, loaded a step before the unit starts.  A
@@ -458,9 +478,9 @@ __device__ __forceinline__ void load_q(const Params& p, const UnitPos& u, int rb
 // loaded when the unit starts -- its first use is 36 MFMAs into the step.
 template <bool KV8, bool Q8>
 struct QNext {
-  static constexpr int kPre = KV8 && !Q8 ? kQkSteps / 2 : kQkSteps;
-  uint4 k[Q8 ? 1 : kPre];
-  uint2 raw[Q8 ? kQkSteps : 1];
+  static constexpr int kPre = KV8 && !Q8 ? kQkSteps / 2 : KV8 ? kQ8Regs : kQkSteps;
+  uint4 k[Q8 && !KV8 ? 1 : kPre];
+  uint2 raw[Q8 && !KV8 ? kQkSteps : 1];
 };
 
 template <int QT, bool KV8, bool Q8>
@@ -469,7 +489,9 @@ __device__ __forceinline__ void prefetch_q(const Params& p, const UnitPos& u, in
   const int64_t e = q_lane_offset(p, u, rb, ok);
 #pragma unroll
   for (int s = 0; s < QNext<KV8, Q8>::kPre; ++s) {
-    if constexpr (Q8)
+    if constexpr (KV8 && Q8)
+      N.k[s] = q8_part(p, e, ok, s);
+    else if constexpr (Q8)
       N.raw[s] = ok ? *(const uint2*)((const uint8_t*)p.q + e + q_dim<KV8>(s, (threadIdx.x & 63) >> 4))
                     : make_uint2(0, 0);
     else
@@ -483,12 +505,12 @@ __device__ __forceinline__ void take_q(const Params& p, const UnitPos& u, int rb
   constexpr int kPre = QNext<KV8, Q8>::kPre;
 #pragma unroll
   for (int s = 0; s < kPre; ++s) {
-    if constexpr (Q8)
+    if constexpr (Q8 && !KV8)
       Q.k[s] = fp8x8_to_16<QT>(N.raw[s]);
     else
       Q.k[s] = N.k[s];
   }
-  if constexpr (kPre < kQkSteps) {
+  if constexpr (kPre < kQkSteps && !(KV8 && Q8)) {
     bool ok;
     const int64_t e = q_lane_offset(p, u, rb, ok);
 #pragma unroll
@@ -511,7 +533,7 @@ struct RowState {
   float m, l;
 };
 
-template <int QT, bool KV8>
+template <int QT, bool KV8, bool Q8>
 __device__ __forceinline__ void score_tile(const Params& p, const UnitPos& u, const RowVis& vis, int lo_last,
                                            int mask_from, const QRegs& Q, const uint8_t* tl, const uint8_t* th,
                                            int rb, int par, int t, Smem<KV8>& sm, RowState& st) {
@@ -520,7 +542,52 @@ __device__ __forceinline__ void score_tile(const Params& p, const UnitPos& u, co
   f32x4 s4[kTB];
 #pragma unroll
   for (int tb = 0; tb < kTB; ++tb) s4[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (KV8) {
+  if constexpr (KV8 && Q8) {
+    // fp8 query and cache: S^T on v_mfma_f32_16x16x128_f8f6f4, K and Q as
+    // bytes.  K fragment (tb, s) of lane (n, g): dims 128 s + 32 g .. + 32 of
+    // row 16 tb + n, i.e. chunks 8 s + 2 g + h (h = 0, 1), chunk c at
+    // 16 (c / 16) + ((c % 16) ^ swz_lo(n)); s = 4: rope chunks 2 g + h of
+    // lanes g < 2 (zeros for the others, whose query bytes are zeros).
+    int kb8[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) kb8[a][h] = n * kLo8Row + 16 * ((8 * a + 2 * g + h) ^ swz_lo(n));
+    const int hb[2] = {n * kHi8Row + 16 * ((2 * (g & 1)) ^ swz8_hi(n)),
+                       n * kHi8Row + 16 * ((2 * (g & 1) + 1) ^ swz8_hi(n))};
+    auto frag = [&](int s, int tb) {
+      uint4 a, b;
+      if (s < 4) {
+        a = *(const uint4*)(tl + tb * 16 * kLo8Row + kb8[s & 1][0] + 256 * (s >> 1));
+        b = *(const uint4*)(tl + tb * 16 * kLo8Row + kb8[s & 1][1] + 256 * (s >> 1));
+      } else {
+        a = *(const uint4*)(th + tb * 16 * kHi8Row + hb[0]);
+        b = *(const uint4*)(th + tb * 16 * kHi8Row + hb[1]);
+        if (g >= 2) a = b = make_uint4(0, 0, 0, 0);
+      }
+      return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    };
+    auto qop = [&](int s) {
+      const uint4 a = Q.k[2 * s], b = Q.k[2 * s + 1];
+      return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    };
+    constexpr int kSteps8 = 5;
+    i32x8 kf[2][kTB];
+#pragma unroll
+    for (int tb = 0; tb < kTB; ++tb) kf[0][tb] = frag(0, tb);
+#pragma unroll
+    for (int s = 0; s < kSteps8; ++s) {
+      if (s + 1 < kSteps8) {
+#pragma unroll
+        for (int tb = 0; tb < kTB; ++tb) kf[(s + 1) & 1][tb] = frag(s + 1, tb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int tb = 0; tb < kTB; ++tb)
+        s4[tb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kf[s & 1][tb], qop(s), s4[tb], 0, 0, 0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else if constexpr (KV8) {
     // fragment pair (tb, sp) of lane (n, g): the 16 bytes of chunk 4 sp + g
     // of row 16 tb + n, i.e. dims 64 sp + 16 g .. + 16 -- K steps 2 sp and
     // 2 sp + 1 (sp = 8: rope chunk g).  Chunk 4 sp + g sits at
@@ -670,7 +737,7 @@ __device__ __forceinline__ void score_role(const Params& p, const SkSched& S, in
       th = slot_hi8(sm, i3);
       i3 = i3 == kHi8Ring - 1 ? 0 : i3 + 1;
     }
-    score_tile<QT, KV8>(p, cur, vis, lo_last, mask_from, Q, slot_lo(sm, i), th, rb, i & 1, t, sm, st);
+    score_tile<QT, KV8, Q8>(p, cur, vis, lo_last, mask_from, Q, slot_lo(sm, i), th, rb, i & 1, t, sm, st);
     if ((t + 1 == cur.uend || t + 1 == x1) && g == 0) sm.ml[i & 1][row] = make_float2(st.m, st.l);
   };
   lds_barrier();            // tile x0 is in LDS

@@ -342,6 +342,18 @@ def test_full_size_sampled_parity(name):
     assert not torch.isnan(got).any()
 
 
+def test_full_size_sampled_parity_fp8_latent():
+    # the fp8 latent workload (fp8 query and cache, 32 sequences of 4096 to
+    # 16384 tokens, 64 heads) on the schedule the benchmark times
+    w = synth.WORKLOADS["mla_fp8"]
+    print("[case] full mla_fp8", flush=True)
+    inp = make(w, seed=1)
+    got = run_gpu(w, inp)
+    idx = _sample(inp["seq_lens_host"], 4)
+    assert_parity(w, got[idx.to(DEV)], run_oracle(w, inp, idx), "full/mla_fp8")
+    assert not torch.isnan(got).any()
+
+
 def test_full_size_sampled_parity_512_sequences():
     # the Llama-3-8B decode shape at 512 sequences: the wide stream-K schedule
     w = synth.WORKLOADS["llama3_8b_gqa"].replace(batch=512)
@@ -624,12 +636,12 @@ MLA_FP8 = MLA_SMALL.replace(kv_dtype=torch.float8_e4m3fn, kv_scale=0.05, kv_gen_
 
 
 @pytest.mark.parametrize("q", ["bf16", "f16", "fp8"])
-@pytest.mark.parametrize("ps", [16, 64])
+@pytest.mark.parametrize("ps", [16, 32, 64, 128])
 @pytest.mark.parametrize("split", [0, 3])
 def test_mla_fp8_cache(q, ps, split):
-    # an e4m3fn latent cache (converted exactly to the operand type as tiles
-    # enter LDS), with a 16-bit query or the quantised (e4m3fn) query of the
-    # latent path, whose output is bfloat16
+    # an e4m3fn latent cache, with a 16-bit query or the quantised (e4m3fn)
+    # query of the latent path, whose output is bfloat16; split 0: stream-K
+    # over 64-token tiles (one to four pages each), split 3: the split grid
     qd = {"bf16": torch.bfloat16, "f16": torch.float16, "fp8": torch.float8_e4m3fn}[q]
     w = MLA_FP8.replace(q_dtype=qd, page_size=ps)
     print(f"[case] mla fp8 cache, q {q}, ps={ps} split={split}", flush=True)
@@ -639,11 +651,18 @@ def test_mla_fp8_cache(q, ps, split):
     assert_parity(w, got, run_oracle(w, inp), f"mla-fp8/q{q}/ps{ps}/split{split}")
 
 
-@pytest.mark.parametrize("variant", ["window_sinks_q8", "spec4_q8", "ragged_q8", "W7_q16"])
+@pytest.mark.parametrize("variant", ["window_sinks_q8", "spec4_q8", "ragged_q8", "W7_q16", "W1_q8",
+                                     "W300_q8", "rows20_q16"])
 def test_mla_fp8_variants(variant):
     base = MLA_FP8.replace(q_dtype=torch.float8_e4m3fn)
     kw, lens = {}, None
-    if variant == "window_sinks_q8":
+    if variant == "W1_q8":          # one workgroup: every unit switch in one share
+        w, kw = base, dict(target_ctas=1)
+    elif variant == "W300_q8":      # more workgroups than tiles of some units
+        w, kw = base.replace(seq_len_range=(1, 400)), dict(target_ctas=300)
+    elif variant == "rows20_q16":   # 20 query rows: partial row blocks in both roles
+        w = MLA_FP8.replace(num_q_heads=20)
+    elif variant == "window_sinks_q8":
         w = base.replace(window=100, sinks=True, seq_len_range=(1, 900), q_scale=1.3)
     elif variant == "spec4_q8":
         w = base.replace(num_q_heads=16, q_seq_len=4, mask="causal", seq_len_range=(4, 700))
