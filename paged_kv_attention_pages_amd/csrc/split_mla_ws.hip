@@ -382,16 +382,17 @@ __device__ __forceinline__ void load_tile(const Params& p, const LoadCursor<KV8>
       load_to_lds(rp, hi_lds + 1024 * pw, voff, 0);
     }
   } else {
+    const i32x4 r0 = rs(c.pid[0]), r1 = rs(c.pid[1]);
     if (whole) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int hf = k >> 2, rr = 4 * (k & 3) + pw;
         const int soff = ((tok0 + 16 * hf + rr) & pmask) * row_bytes + head_off;
-        load_to_lds(rs(c.pid[hf]), lo_lds + hf * kHalfBytes + rr * kLoBytes, ll.lo[k & 3], soff);
+        load_to_lds(hf ? r1 : r0, lo_lds + hf * kHalfBytes + rr * kLoBytes, ll.lo[k & 3], soff);
       }
       const int hf = pw >> 1;
       const int soff = ((tok0 + 16 * hf + 8 * (pw & 1)) & pmask) * row_bytes + head_off;
-      load_to_lds(rs(hf ? c.pid[1] : c.pid[0]), lo_lds + hf * kHalfBytes + kHiOff + 8 * (pw & 1) * kHiBytes,
+      load_to_lds(hf ? r1 : r0, lo_lds + hf * kHalfBytes + kHiOff + 8 * (pw & 1) * kHiBytes,
                   (ll.rope_row - 8 * (pw & 1)) * row_bytes + ll.rope_col, soff);
     } else {
 #pragma unroll
@@ -400,13 +401,13 @@ __device__ __forceinline__ void load_tile(const Params& p, const LoadCursor<KV8>
         const int tok = tok0 + 16 * hf + rr;
         const bool in = tok >= c.u.lo && tok < c.u.L;
         const int voff = in ? (tok & pmask) * row_bytes + head_off + ll.lo[k & 3] : (int)0x80000000u;
-        load_to_lds(rs(c.pid[hf]), lo_lds + hf * kHalfBytes + rr * kLoBytes, voff, 0);
+        load_to_lds(hf ? r1 : r0, lo_lds + hf * kHalfBytes + rr * kLoBytes, voff, 0);
       }
       const int hf = pw >> 1;
       const int tok = tok0 + 16 * hf + ll.rope_row;
       const bool in = tok >= c.u.lo && tok < c.u.L;
       const int voff = in ? (tok & pmask) * row_bytes + head_off + ll.rope_col : (int)0x80000000u;
-      load_to_lds(rs(hf ? c.pid[1] : c.pid[0]), lo_lds + hf * kHalfBytes + kHiOff + 8 * (pw & 1) * kHiBytes, voff, 0);
+      load_to_lds(hf ? r1 : r0, lo_lds + hf * kHalfBytes + kHiOff + 8 * (pw & 1) * kHiBytes, voff, 0);
     }
   }
 }

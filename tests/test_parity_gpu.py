@@ -854,23 +854,26 @@ def test_device_scale_arguments_checked():
 # ---------------------------------------------------------------- fp8 output (rcp_out_scale)
 
 @pytest.mark.parametrize("rcp", [1.0, 6.0])
-@pytest.mark.parametrize("mode", ["sk", "grid", "valu", "one_launch"])
+@pytest.mark.parametrize("mode", ["sk", "grid", "valu", "one_launch", "latent_sk", "latent_grid"])
 def test_fp8_output_with_rcp_out_scale(mode, rcp):
     # an fp8 cache may write an fp8 output holding round(out * rcp_out_scale);
     # the decoded output / rcp is within the bound plus half an E4M3 step
-    w = SMALL["fp8"]
+    # (latent: fp8 query and cache, whole units from the split kernel and cut
+    # ones from the combine)
+    w = MLA_FP8.replace(q_dtype=torch.float8_e4m3fn) if mode.startswith("latent") else SMALL["fp8"]
     print(f"[case] fp8 output {mode} rcp={rcp}", flush=True)
     inp = make(w, seed=95)
     B = inp["q"].shape[0]
     out = torch.full((B, w.q_seq_len, w.num_q_heads, w.head_dim_v), float("nan"),
                      dtype=torch.float8_e4m3fn, device=DEV)
     kw = {"sk": {}, "grid": {"split_pages": 3}, "valu": {"path": "valu"},
-          "one_launch": {"single_launch": True, "target_ctas": 7}}[mode]
+          "one_launch": {"single_launch": True, "target_ctas": 7},
+          "latent_sk": {"target_ctas": 5}, "latent_grid": {"split_pages": 3}}[mode]
     pkv.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"], inp["seq_lens"],
                     out, num_kv_heads=w.num_kv_heads, page_size=w.page_size, sinks=inp["sinks"],
                     q_scale=w.q_scale, kv_scale=w.kv_scale, sliding_win_size=w.window,
                     kv_layout=w.kv_layout, q_seq_len=w.q_seq_len, mask=inp["mask"],
-                    rcp_out_scale=rcp, **kw)
+                    rcp_out_scale=rcp, head_dim_v=w.head_dim_v, **kw)
     torch.cuda.synchronize()
     ref = run_oracle(w, inp)
     got = out.cpu().to(torch.float64) / rcp
