@@ -744,13 +744,15 @@ def test_stream_k_wide_batches(kind, B):
         assert torch.equal(got[L == 0].float().cpu(), torch.zeros_like(got[L == 0].float().cpu()))
 
 
-@pytest.mark.parametrize("name", ["gqa", "spec", "mla", "fp8_unit_waves"])
+@pytest.mark.parametrize("name", ["gqa", "spec", "mla", "fp8_unit_waves", "mla_fp8"])
 def test_graph_replay_matches_eager(name):
     # a captured call (workspace passed in, so nothing is allocated inside the
     # capture) replayed several times, with eager work between the replays;
     # fp8_unit_waves: a window and two units per CU (one wave per unit)
     kw = dict(num_cus=2) if name == "fp8_unit_waves" else {}
     w = MLA_SMALL if name == "mla" else SMALL[name.split("_")[0]]
+    if name == "mla_fp8":
+        w = MLA_FP8.replace(q_dtype=torch.float8_e4m3fn)
     print(f"[case] graph replay {name}", flush=True)
     inp = make(w, seed=99)
     plan = pkv.query_plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
@@ -760,7 +762,7 @@ def test_graph_replay_matches_eager(name):
                           q_seq_len=w.q_seq_len, **kw)
     ws = torch.empty(max(plan["workspace_bytes"], 256), dtype=torch.uint8, device=DEV)
     out = torch.full((w.batch, w.q_seq_len, w.num_q_heads, w.head_dim_v), float("nan"),
-                     dtype=w.q_dtype, device=DEV)
+                     dtype=out_dtype(w), device=DEV)
 
     def call():
         pkv.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"],

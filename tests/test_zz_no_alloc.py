@@ -67,6 +67,8 @@ CASES = {
     "gqa_split_grid": dict(split_pages=2),
     # a window and two units per CU: one wave per (sequence, KV head)
     "fp8_unit_waves": dict(num_cus=2),
+    # fp8 query and latent cache (64-token tiles), four workgroups
+    "mla_fp8": dict(target_ctas=4),
 }
 
 
@@ -76,6 +78,9 @@ def test_noalloc_matches_workspace_entry_point(case):
     name = case.split("_")[0]
     kw = CASES[case]
     w1 = SMALL[name]
+    if case == "mla_fp8":
+        w1 = w1.replace(q_dtype=torch.float8_e4m3fn, kv_dtype=torch.float8_e4m3fn, kv_scale=0.05,
+                        kv_gen_scale=1.0 / 0.05)
     lo, hi = w1.seq_len_range
     w2 = w1.replace(batch=max(1, w1.batch - 2), seq_len_range=(lo, max(lo, hi // 3)))
     for step, (w, seed) in enumerate(((w1, 201), (w2, 202))):
