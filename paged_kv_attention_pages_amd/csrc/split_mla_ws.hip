@@ -22,9 +22,10 @@
 //     slice held in registers, runs the rows' online softmax, and leaves the
 //     16-bit probabilities and the rows' rescale factors in LDS;
 //   P.V waves 4..7 (one per SIMD): wave (rh, dh) takes rows 32 rh .. + 31 and
-//     value dims 256 dh .. + 255 of tile t: it rescales its accumulators and
-//     adds O^T (256 dims x 32 rows) += V^T . P^T as 32x32x16 MFMAs with V^T
-//     from transposed LDS reads; these waves also issue the tile loads.
+//     value dims 256 dh .. + 255 of tile t (of an fp8 tile: wave w takes all
+//     64 rows and dims 128 w .. + 127): it rescales its accumulators and adds
+//     O^T += V^T . P^T as 32x32x16 MFMAs with V^T from transposed LDS reads;
+//     these waves also issue the tile loads.
 // One barrier per step.  For a 16-bit tile the LDS serves 144 KB of K reads,
 // 64 KB of V reads and 12 KB of probability traffic -- against about 290 KB
 // read and 52 KB written when every wave did both products for its own rows.
