@@ -678,6 +678,32 @@ def test_mla_fp8_variants(variant):
     assert_parity(w, got, run_oracle(w, inp), f"mla-fp8/{variant}")
 
 
+@pytest.mark.parametrize("split", [0, 3])
+def test_mla_fp8_query_matches_its_bf16_image(split):
+    # An fp8 query takes the fp8 matrix instruction for the scores on the
+    # stream-K kernel (inexact sums, ~1e-4 of the products' magnitudes) and
+    # the exact conversion on the split grid; the same query as bf16 (an exact
+    # image) goes through the exact route.  On the grid the outputs are
+    # identical; on stream-K they differ by the fp8 sums' error, which peaky
+    # attention (large logits) carries into the output -- bounded here by a
+    # quarter of the parity tolerance.
+    w = MLA_FP8.replace(q_dtype=torch.float8_e4m3fn, batch=6, seq_len_range=(1, 2000))
+    print(f"[case] fp8 query vs its bf16 image, split={split}", flush=True)
+    inp = make(w, seed=71)
+    got8 = run_gpu(w, inp, split_pages=split).float()
+    w16 = w.replace(q_dtype=torch.bfloat16)
+    inp16 = dict(inp, q=inp["q"].to(torch.bfloat16))
+    got16 = run_gpu(w16, inp16, split_pages=split).float()
+    diff = (got8 - got16).abs().max().item()
+    rms = got16.pow(2).mean().sqrt().item()
+    print(f"[parity] fp8-vs-bf16-query split={split} max_diff={diff:.3e} rms={rms:.3e}", flush=True)
+    if split:
+        assert diff == 0.0          # the same exact route
+    else:
+        assert diff <= 0.25 * tol_for(w)
+    assert_parity(w, got8.to(torch.bfloat16), run_oracle(w, inp), f"q8-image/split{split}")
+
+
 def test_mla_fp8_query_rejected_off_the_latent_path():
     w = SMALL["fp8"].replace(q_dtype=torch.float8_e4m3fn)
     inp = make(w, seed=100)
