@@ -73,8 +73,9 @@ struct Plan {
   size_t ws_ml_off;    // offset of (max, sum) pairs
   size_t ws_cnt_off;   // offset of the per-unit counters (single-launch merge)
   bool fused;          // cut units merged in the split kernel (no combine launch)
-  bool lat_ws;         // latent stream-K with separate score / P.V waves (16-bit cache)
+  bool lat_ws;         // latent stream-K with separate score / P.V waves
   bool unit_aligned;   // matrix-core stream-K over B * Hkv waves, one per unit when even
+  bool unit_whole;     // matrix-core, one wave per unit always, nothing cut (no combine)
   size_t ws_bytes;
 };
 
@@ -224,6 +225,7 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
   pl->fused = false;
   pl->lat_ws = false;
   pl->unit_aligned = false;
+  pl->unit_whole = false;
   pl->ws_cnt_off = 0;
   // Stream-K schedule (matrix-core path, batch <= 256, no forced split size):
   // persistent waves (measured best: one per SIMD for 16-bit caches, each
@@ -278,6 +280,28 @@ pkv_status make_plan(const pkv_dims* d, int Hkv, int ps, int layout, int window,
     // it is used when no wave's share can exceed 8 tiles.  The latent-cache
     // kernel leaves the merge of its 64-row partials to the combine kernel.
     const int mode = opts ? opts->merge_mode : 0;
+    // Short sequences: when no unit can span more than 17 tiles (at most 256
+    // cached tokens a sequence, or within the window), one wave per unit
+    // streams it whole in one launch -- nothing is cut, no partial is
+    // written and no combine runs -- and the units' start latencies (query,
+    // page ids, first tiles) overlap instead of following one another in a
+    // wave's share.  Up to eight units per CU.
+    int64_t span = pages_max * ps;   // most tokens a unit can see
+    if (window > 0) span = std::min<int64_t>(span, (int64_t)window + Tq - 1);
+    if (path == PKV_PATH_MFMA && mode == 0 && !(opts && opts->target_ctas > 0) &&
+        cdiv(span, 16) + 1 <= 17 && units <= 8 * (int64_t)cus) {
+      pl->unit_whole = true;
+      pl->sk_waves = (int)units;
+      pl->sk_hb = 1;
+      const int64_t res = std::min<int64_t>(8, units / cus);
+      for (int h = (int)std::min<int64_t>(res, Hkv); h > 1; --h)
+        if (Hkv % h == 0) {
+          pl->sk_hb = h;
+          break;
+        }
+      pl->ws_o_bytes = pl->ws_ml_off = pl->ws_bytes = 0;
+      return PKV_OK;
+    }
     // With a window every unit spans at most cdiv(window + Tq - 1, 16) + 1
     // tiles, and where the sequences reach past the window the units are of
     // (nearly) equal length.  Then one wave per whole unit is as balanced as
@@ -413,7 +437,7 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
   p.qk_unit = (float)(1.4426950408889634 / std::sqrt((double)Dk));
   p.fused = pl.fused ? 1 : 0;
   p.ws_lanes = pl.lat_ws ? 1 : 0;
-  p.sk_units = pl.unit_aligned ? 1 : 0;
+  p.sk_units = pl.unit_whole ? 2 : pl.unit_aligned ? 1 : 0;
   p.out_fp8 = out_fp8 ? 1 : 0;
   p.rcp_out_scale = rcp_out;
   p.ws_cnt = pl.fused ? (unsigned long long*)((char*)workspace + pl.ws_cnt_off) : nullptr;
@@ -438,7 +462,7 @@ pkv_status decode(const void* q, const void* k, const void* v, const int32_t* pa
     e = hipEventRecord((hipEvent_t)opts->split_event, s);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "event record failed: %s", hipGetErrorString(e));
   }
-  if (!pl.fused) {
+  if (!pl.fused && !pl.unit_whole) {
     // an fp8 query's output is bfloat16
     e = pkv::launch_combine(d->q_dtype == PKV_FP8_E4M3 ? PKV_BF16 : d->q_dtype, p, s);
     if (e != hipSuccess) return fail(PKV_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
@@ -472,7 +496,7 @@ pkv_status pkv_query_plan(const pkv_dims* dims, int num_kv_heads, int page_size,
       pl.sk_waves > 0 ? pl.sk_waves : pl.max_splits * num_kv_heads * dims->batch;
   info->num_cus = pl.num_cus;
   info->workspace_bytes = pl.ws_bytes;
-  info->single_launch = pl.fused ? 1 : 0;
+  info->single_launch = pl.fused || pl.unit_whole ? 1 : 0;
   info->waves_per_workgroup = pl.path == PKV_PATH_MFMA_MLA ? 8 : pl.sk_waves > 0 ? pl.sk_hb : 1;
   g_err.clear();
   return PKV_OK;

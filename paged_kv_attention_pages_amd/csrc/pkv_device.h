@@ -54,9 +54,10 @@ struct Params {
   // latent stream-K partials in the P.V waves' register order, 64 rows a
   // slot (split_mla_ws.hip; merged by combine_lat_kernel)
   int ws_lanes;
-  // matrix-core stream-K over sk_waves == B * Hkv waves that, when the units
-  // are even (sk_units_even), give each unit one wave and cut nothing (the
-  // combine then finds nothing to merge); otherwise equal shares as usual
+  // matrix-core stream-K over sk_waves == B * Hkv waves: 1 = when the units
+  // are even (sk_units_even) each unit gets one wave and nothing is cut (the
+  // combine then finds nothing to merge), otherwise equal shares as usual;
+  // 2 = each unit gets one wave always (short sequences; no combine runs)
   int sk_units;
 };
 

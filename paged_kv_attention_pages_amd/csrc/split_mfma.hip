@@ -538,9 +538,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   // per-lane buffer resource costs a loop around every load)
   w = __builtin_amdgcn_readfirstlane(w);
   int64_t x0, x1;
-  if (p.sk_units && sk_units_even(p, S)) {
+  if (p.sk_units == 2 || (p.sk_units == 1 && sk_units_even(p, S))) {
     // one wave per unit: wave w = kvh * B + b streams all of unit (b, kvh)
-    // (the KV-head-major unit order); an empty unit gets zeros
+    // (the KV-head-major unit order); an empty unit gets zeros.  sk_units 2:
+    // always (short sequences), 1: when the units are even
     if (w >= p.sk_waves) return;
     const int kvh = w / p.B, b = w - kvh * p.B;
     int pre, n;

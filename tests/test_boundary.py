@@ -134,6 +134,25 @@ def test_plan_stream_k():
     assert plan(batch=257, **lat)["split_pages"] > 0
 
 
+def test_plan_one_wave_per_short_unit():
+    # caches of at most 256 tokens a sequence (or a window that short): one
+    # wave per (sequence, KV head), whole, one launch, no workspace
+    short = plan(batch=2, num_q_heads=4, num_kv_heads=1, pages_per_seq=16, page_size=16)
+    assert short["ctas_per_split_grid"] == 2 and short["single_launch"] == 1
+    assert short["workspace_bytes"] == 0 and short["split_pages"] == 0
+    assert plan(batch=64, pages_per_seq=4, page_size=64)["workspace_bytes"] == 0          # 256 tokens
+    assert plan(batch=64, pages_per_seq=5, page_size=64)["workspace_bytes"] > 0           # 320
+    assert plan(batch=64, pages_per_seq=128, page_size=64, window=200)["workspace_bytes"] == 0
+    assert plan(batch=64, pages_per_seq=4, page_size=64, num_cus=2)["workspace_bytes"] > 0  # > 8 / CU
+    wide = plan(batch=64, pages_per_seq=4, page_size=64)     # 512 units: 2 per CU, 2 heads a group
+    assert wide["ctas_per_split_grid"] == 512 and wide["waves_per_workgroup"] == 2
+    # forced merges and wave counts keep their plans
+    assert plan(batch=64, pages_per_seq=4, page_size=64, target_ctas=100)["workspace_bytes"] > 0
+    mla = plan(batch=2, num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
+               pages_per_seq=4, page_size=64)
+    assert mla["workspace_bytes"] > 0                      # the latent path keeps stream-K
+
+
 def test_plan_one_wave_per_windowed_unit():
     # with a window, the merge chosen by default and no forced wave count, a
     # batch of at least two units per CU gets B * Hkv waves (the kernels run

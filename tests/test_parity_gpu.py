@@ -924,6 +924,37 @@ def test_fp8_output_needs_an_fp8_cache():
                         kv_layout=w.kv_layout)
 
 
+@pytest.mark.parametrize("kind, lens, kw", [
+    ("tiny", [37, 100], {}),
+    ("gqa", [0, 1, 255, 256, 17, 128, 64, 200], {}),
+    ("gqa", [0, 1, 255, 256, 17, 128, 64, 200], {"num_cus": 8}),     # 8 units a CU: 8 heads a group
+    ("gqa", [0, 1, 255, 256, 17, 128, 64, 200], {"num_cus": 16}),    # 4 heads a group
+    ("fp8", [700, 2000, 5, 0, 1200], {}),                              # window 200: short spans
+    ("spec", [4, 5, 130, 256], {}),
+    ("d64", [1, 64, 65, 250], {}),
+    ("d256", [1, 64, 65, 250], {}),
+])
+def test_short_sequences_one_wave_per_unit(kind, lens, kw):
+    # every unit spans at most 17 tiles (256 cached tokens, or a window that
+    # short): one wave per unit, whole, in one launch with no workspace
+    base = {"tiny": SMALL["tiny"], "gqa": SMALL["gqa"], "fp8": SMALL["fp8"].replace(window=200),
+            "spec": SMALL["spec"],
+            "d64": SMALL["gqa"].replace(head_dim_qk=64, head_dim_v=64),
+            "d256": SMALL["gqa"].replace(head_dim_qk=256, head_dim_v=256)}[kind]
+    w = base.replace(batch=len(lens), seq_len_range=(1, max(lens)))
+    print(f"[case] short units {kind} lens={lens} {kw}", flush=True)
+    inp = make(w, seed=70 + len(lens), seq_lens=lens)
+    plan = pkv.query_plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                          head_dim_qk=w.head_dim_qk, head_dim_v=w.head_dim_v,
+                          pages_per_seq=inp["page_table"].shape[1], page_size=w.page_size,
+                          q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, window=w.window,
+                          q_seq_len=w.q_seq_len, **kw)
+    assert plan["single_launch"] == 1 and plan["workspace_bytes"] == 0, plan
+    assert plan["ctas_per_split_grid"] == w.batch * w.num_kv_heads
+    got = run_gpu(w, inp, **kw)
+    assert_parity(w, got, run_oracle(w, inp), f"short/{kind}")
+
+
 def _units_even(w, lens):
     """Which schedule the one-wave-per-unit plan runs: with 16-token tiles of
     the visible span [max(0, L - Tq + 1 - window), L), one wave per unit
