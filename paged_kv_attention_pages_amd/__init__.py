@@ -162,9 +162,12 @@ def _current_stream(dev: int) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
 
+_get_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
 def _call_on(dev: int, fn, *args):
     """fn(*args) with device `dev` current (switching only when it is not)."""
-    if torch.cuda.current_device() == dev:
+    if (_get_device() if _get_device is not None else torch.cuda.current_device()) == dev:
         return fn(*args)
     with torch.cuda.device(dev):
         return fn(*args)
@@ -261,51 +264,62 @@ def _workspace(device, stream: int, nbytes: int) -> torch.Tensor:
 
 def _shape_checks(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size,
                   kv_layout, q_seq_len, head_dim_v, mask):
-    B, Hq, Dk = q.shape[0], q.shape[-2], q.shape[-1]
+    """Shape, dtype, layout and device checks of a decode call; returns q's
+    (B, Hq, Dk), the table width and the pages in the cache.  Each tensor's
+    shape and dtype are read once (a call on small inputs is host-bound)."""
+    qs, ks, pts = q.shape, k_cache.shape, page_table.shape
+    B, Hq, Dk = qs[0], qs[-2], qs[-1]
     if q.numel() != B * q_seq_len * Hq * Dk:
-        raise PkvError(1, f"q of shape {tuple(q.shape)} does not hold batch x q_seq_len "
+        raise PkvError(1, f"q of shape {tuple(qs)} does not hold batch x q_seq_len "
                           f"({q_seq_len}) x num_q_heads x head_dim elements (beam width 1 only)")
     if kv_layout not in _LAYOUT:
         raise PkvError(1, f"kv_layout must be 'NHD' or 'HND', got {kv_layout!r}")
-    if k_cache.dim() != 4:
-        raise PkvError(1, f"k_cache must be 4-D, got shape {tuple(k_cache.shape)}")
+    if len(ks) != 4:
+        raise PkvError(1, f"k_cache must be 4-D, got shape {tuple(ks)}")
     ps_dim, h_dim = (1, 2) if kv_layout == "NHD" else (2, 1)
-    if k_cache.shape[ps_dim] != page_size or k_cache.shape[h_dim] != num_kv_heads \
-            or k_cache.shape[3] != Dk:
-        raise PkvError(1, f"k_cache shape {tuple(k_cache.shape)} does not match {kv_layout} with "
+    if ks[ps_dim] != page_size or ks[h_dim] != num_kv_heads or ks[3] != Dk:
+        raise PkvError(1, f"k_cache shape {tuple(ks)} does not match {kv_layout} with "
                           f"page_size {page_size}, num_kv_heads {num_kv_heads}, head_dim {Dk}")
+    kdt = k_cache.dtype
     if v_cache is not k_cache and v_cache.data_ptr() != k_cache.data_ptr():
-        if tuple(v_cache.shape[:3]) != tuple(k_cache.shape[:3]) or v_cache.shape[3] != head_dim_v:
-            raise PkvError(1, f"v_cache shape {tuple(v_cache.shape)} does not match k_cache "
-                              f"{tuple(k_cache.shape)} with head_dim_v {head_dim_v}")
-        if v_cache.dtype != k_cache.dtype:
+        vs = v_cache.shape
+        if vs[:3] != ks[:3] or vs[3] != head_dim_v:
+            raise PkvError(1, f"v_cache shape {tuple(vs)} does not match k_cache "
+                              f"{tuple(ks)} with head_dim_v {head_dim_v}")
+        if v_cache.dtype != kdt:
             raise PkvError(1, "k_cache and v_cache must have the same dtype")
-    if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.shape[0] != B:
+    if page_table.dtype != torch.int32 or len(pts) != 2 or pts[0] != B:
         raise PkvError(1, f"page_table must be int32 [batch, pages_per_seq], got "
-                          f"{page_table.dtype} {tuple(page_table.shape)}")
+                          f"{page_table.dtype} {tuple(pts)}")
     if seq_lens.dtype not in (torch.int32, torch.uint32) or seq_lens.numel() != B:
         raise PkvError(1, f"seq_lens must be uint32 (or int32) [batch] or [batch, 1], got "
                           f"{seq_lens.dtype} {tuple(seq_lens.shape)}")
     # an fp8 query's output is bfloat16 (or the fp8 cache's dtype)
-    out16 = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
-    out_ok = output.dtype == out16 or (output.dtype in (torch.float8_e4m3fn, torch.uint8)
-                                       and k_cache.dtype in (torch.float8_e4m3fn, torch.uint8))
+    qdt, odt = q.dtype, output.dtype
+    out16 = torch.bfloat16 if qdt == torch.float8_e4m3fn else qdt
+    out_ok = odt == out16 or (odt in (torch.float8_e4m3fn, torch.uint8)
+                              and kdt in (torch.float8_e4m3fn, torch.uint8))
     if not out_ok or output.numel() != B * q_seq_len * Hq * head_dim_v:
         raise PkvError(1, f"output must have q's dtype (bfloat16 for an fp8 query, or the fp8 "
                           f"cache's) and batch x q_seq_len x num_q_heads x head_dim_v elements, "
-                          f"got {output.dtype} {tuple(output.shape)}")
+                          f"got {odt} {tuple(output.shape)}")
     if mask is not None and q_seq_len > 1:
         want = (B, q_seq_len, ((q_seq_len + 31) // 32) * 2)
         if mask.dtype not in (torch.uint16, torch.int16) or tuple(mask.shape) != want:
             raise PkvError(1, f"mask must be uint16 {want}, got {mask.dtype} {tuple(mask.shape)}")
+    # q is a device tensor (checked by the caller), so dev >= 0 and a host
+    # tensor (get_device() == -1) fails the comparison
     dev = q.get_device()
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                     ("page_table", page_table), ("seq_lens", seq_lens), ("output", output),
                     ("mask", mask)):
-        if t is not None and not t.is_contiguous():
+        if t is None:
+            continue
+        if not t.is_contiguous():
             raise PkvError(1, f"{name} must be contiguous")
-        if t is not None and (not t.is_cuda or t.get_device() != dev):
+        if t.get_device() != dev:
             raise PkvError(1, f"{name} is on {t.device}, q on {q.device}")
+    return B, Hq, Dk, pts[1], ks[0]
 
 
 def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buffer=None, *,
@@ -349,11 +363,11 @@ def decode_attn(q, k_cache, v_cache, page_table, seq_lens, output, workspace_buf
     extra = () if opts is None else (ctypes.byref(opts),)
     for attempt in (0, 1):
         d.workspace_bytes = workspace_buffer.numel() * workspace_buffer.element_size()
-        args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens),
-                _ptr(output), _ptr(workspace_buffer), num_kv_heads, page_size, _LAYOUT[kv_layout],
-                _ptr(sinks), float(q_scale), float(kv_scale), int(sliding_win_size),
-                int(q_seq_len), _ptr(mask if q_seq_len > 1 else None), stream,
-                ctypes.byref(d)) + extra
+        args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), page_table.data_ptr(),
+                seq_lens.data_ptr(), output.data_ptr(), workspace_buffer.data_ptr(),
+                num_kv_heads, page_size, _LAYOUT[kv_layout], _ptr(sinks), q_scale, kv_scale,
+                int(sliding_win_size), int(q_seq_len), _ptr(mask if q_seq_len > 1 else None),
+                stream, ctypes.byref(d)) + extra
         st = _call_on(dev, fn, *args)
         if st != PKV_ERR_WORKSPACE_TOO_SMALL or not own_ws or attempt:
             break
@@ -372,19 +386,29 @@ def _decode_prep(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads
     """Argument checks and the C structs of a decode call (no device work)."""
     if not q.is_cuda:
         raise PkvError(1, "decode_attn runs on the GPU only: q must be a device tensor")
-    _shape_checks(q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size,
-                  kv_layout, q_seq_len, head_dim_v, mask)
+    B, Hq, Dk, pages_per_seq, num_pages = _shape_checks(
+        q, k_cache, v_cache, page_table, seq_lens, output, num_kv_heads, page_size, kv_layout,
+        q_seq_len, head_dim_v, mask)
     if sinks is not None:
-        if sinks.dtype != torch.float32 or sinks.numel() != q.shape[-2] or not sinks.is_contiguous():
+        if sinks.dtype != torch.float32 or sinks.numel() != Hq or not sinks.is_contiguous():
             raise PkvError(1, "sinks must be contiguous float32 [num_kv_heads, head_group_ratio]")
     ev = None if split_event is None else split_event.cuda_event
-    q_scale, q_scale_dev = _scale_arg(q_scale, "q_scale", q.device)
-    kv_scale, kv_scale_dev = _scale_arg(kv_scale, "kv_scale", q.device)
+    q_scale_dev = kv_scale_dev = None
+    if isinstance(q_scale, torch.Tensor):
+        q_scale, q_scale_dev = _scale_arg(q_scale, "q_scale", q.device)
+    if isinstance(kv_scale, torch.Tensor):
+        kv_scale, kv_scale_dev = _scale_arg(kv_scale, "kv_scale", q.device)
     out_fp8 = output.dtype in (torch.float8_e4m3fn, torch.uint8)
     opts = _options(path, split_pages, num_cus, target_ctas, ev, q_scale_dev, kv_scale_dev,
                     single_launch, out_fp8, rcp_out_scale)
-    d = _dims(q, k_cache, page_table, head_dim_v, q_seq_len)
-    return opts, d, q_scale, kv_scale
+    qdt, kdt = q.dtype, k_cache.dtype
+    if qdt not in (torch.float16, torch.bfloat16, torch.float8_e4m3fn):
+        raise PkvError(1, f"q dtype must be float16, bfloat16 or float8_e4m3fn (latent cache), "
+                          f"got {qdt}")
+    if kdt not in _DTYPE:
+        raise PkvError(1, f"unsupported KV cache dtype {kdt}")
+    d = Dims(B, Hq, Dk, head_dim_v, pages_per_seq, num_pages, _DTYPE[qdt], _DTYPE[kdt], 0)
+    return opts, d, float(q_scale), float(kv_scale)
 
 
 def decode_attn_noalloc(q, k_cache, v_cache, page_table, seq_lens, output, *, num_kv_heads,

@@ -933,6 +933,7 @@ def test_fp8_output_needs_an_fp8_cache():
     ("spec", [4, 5, 130, 256], {}),
     ("d64", [1, 64, 65, 250], {}),
     ("d256", [1, 64, 65, 250], {}),
+    ("wide", [(37 * i) % 257 for i in range(600)], {}),                # 600 sequences: wide schedule
 ])
 def test_short_sequences_one_wave_per_unit(kind, lens, kw):
     # every unit spans at most 17 tiles (256 cached tokens, or a window that
@@ -940,9 +941,10 @@ def test_short_sequences_one_wave_per_unit(kind, lens, kw):
     base = {"tiny": SMALL["tiny"], "gqa": SMALL["gqa"], "fp8": SMALL["fp8"].replace(window=200),
             "spec": SMALL["spec"],
             "d64": SMALL["gqa"].replace(head_dim_qk=64, head_dim_v=64),
-            "d256": SMALL["gqa"].replace(head_dim_qk=256, head_dim_v=256)}[kind]
+            "d256": SMALL["gqa"].replace(head_dim_qk=256, head_dim_v=256),
+            "wide": SMALL["gqa"].replace(num_q_heads=8, num_kv_heads=2)}[kind]
     w = base.replace(batch=len(lens), seq_len_range=(1, max(lens)))
-    print(f"[case] short units {kind} lens={lens} {kw}", flush=True)
+    print(f"[case] short units {kind} lens={lens[:8]} ({len(lens)}) {kw}", flush=True)
     inp = make(w, seed=70 + len(lens), seq_lens=lens)
     plan = pkv.query_plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                           head_dim_qk=w.head_dim_qk, head_dim_v=w.head_dim_v,
