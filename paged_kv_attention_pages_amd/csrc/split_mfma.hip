@@ -229,10 +229,12 @@ __device__ __forceinline__ void setup_unit(const Params& p, int b, int kvh, Unit
 
 // Stream the sequence tiles [tile_from, tile_to) of the unit into A.  Runs of
 // at most 64 pages share one vector load of their page ids (one per lane);
-// each run goes through the NS-stage pipeline.
-template <int QT, int KT, int D>
+// each run goes through the NS-stage pipeline.  With PRE, page0_ids holds
+// the unit's page ids from page 0 on (lane l: page l, loaded early by the
+// caller) and serves a run that starts at page 0.
+template <int QT, int KT, int D, bool PRE = false>
 __device__ __forceinline__ void stream_tiles(const Params& p, const Unit<KT, D>& U, int tile_from,
-                                             int tile_to, Acc<D>& A) {
+                                             int tile_to, Acc<D>& A, int page0_ids = -1) {
   using TT = Tile<KT, D>;
   constexpr int NS = TT::STAGES, DT = TT::DT;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
@@ -247,8 +249,11 @@ __device__ __forceinline__ void stream_tiles(const Params& p, const Unit<KT, D>&
     const int run_end = min(tile_to, (st.pg_begin + 64) * tiles_per_page);
     const int pg_last = (run_end - 1) / tiles_per_page;
     st.tile_end = run_end;
-    st.my_page = lane <= pg_last - st.pg_begin
-                     ? p.page_table[(int64_t)U.b * p.pps + st.pg_begin + lane] : -1;
+    if (PRE && st.pg_begin == 0)
+      st.my_page = lane <= pg_last ? page0_ids : -1;
+    else
+      st.my_page = lane <= pg_last - st.pg_begin
+                       ? p.page_table[(int64_t)U.b * p.pps + st.pg_begin + lane] : -1;
     TT buf[NS];
 #pragma unroll
     for (int k = 0; k < NS - 1; ++k) {
@@ -522,8 +527,6 @@ template <int QT, int KT, int D, bool FUSED, int SC>
 // architected VGPRs instead of moving them through AGPRs every tile)
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void split_mfma16_sk_kernel(Params p) {
   resolve_scales(p);
-  const SkSchedC<SC> S = sk_schedule<SC>(p);
-  const int W = sk_waves_eff(S.T, p.sk_waves);
   // workgroup (head group hg, position j) of sk_hb waves: wave i takes share
   // j of KV head hg * sk_hb + i's part of the tile stream (W / Hkv waves per
   // head), i.e. the same tokens as its neighbours, of another KV head
@@ -537,11 +540,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   // registers (a value derived from threadIdx counts as per-lane, and a
   // per-lane buffer resource costs a loop around every load)
   w = __builtin_amdgcn_readfirstlane(w);
+  if (p.sk_units == 2) {
+    // short units (at most 17 tiles): wave w = kvh * B + b streams all of
+    // unit (b, kvh) and needs no schedule, so its first memory round trip
+    // fetches the length, the query rows and the first page ids together
+    if (w >= p.sk_waves) return;
+    const int kvh = w / p.B, b = w - kvh * p.B, lane = threadIdx.x & 63;
+    const int page0_ids = lane < p.pps ? p.page_table[(int64_t)b * p.pps + lane] : -1;
+    Unit<KT, D> U;
+    setup_unit<KT, D>(p, b, kvh, U);
+    int tile0;
+    const int n = seq_tiles(p, b, &tile0);
+    if (n == 0) {
+      zero_unit(p, b, kvh);
+      return;
+    }
+    Acc<D> A;
+    reset<D>(A);
+    stream_tiles<QT, KT, D, true>(p, U, tile0, tile0 + n, A, page0_ids);
+    finish_unit<QT, KT, D>(p, U, A, true, 0);
+    return;
+  }
+  const SkSchedC<SC> S = sk_schedule<SC>(p);
+  const int W = sk_waves_eff(S.T, p.sk_waves);
   int64_t x0, x1;
-  if (p.sk_units == 2 || (p.sk_units == 1 && sk_units_even(p, S))) {
-    // one wave per unit: wave w = kvh * B + b streams all of unit (b, kvh)
-    // (the KV-head-major unit order); an empty unit gets zeros.  sk_units 2:
-    // always (short sequences), 1: when the units are even
+  if (p.sk_units == 1 && sk_units_even(p, S)) {
+    // one wave per unit when the units are even: wave w = kvh * B + b
+    // streams all of unit (b, kvh) (the KV-head-major unit order); an empty
+    // unit gets zeros
     if (w >= p.sk_waves) return;
     const int kvh = w / p.B, b = w - kvh * p.B;
     int pre, n;
