@@ -168,8 +168,10 @@ typedef struct pkv_plan_info {
   int32_t ctas_per_split_grid; /* workgroups launched by the split kernel   */
   int32_t num_cus;
   uint64_t workspace_bytes;    /* bytes the call needs                      */
-  int32_t single_launch;       /* 1: the split kernel merges its partials
-                                  itself (no combine kernel); ABI 3         */
+  int32_t single_launch;       /* 1: one launch, no combine kernel: the
+                                  split kernel merges its partials itself,
+                                  or (short sequences) gives each (sequence,
+                                  KV head) one wave and cuts nothing; ABI 3 */
   int32_t waves_per_workgroup; /* matrix-core stream-K: waves per workgroup,
                                   each streaming the same tokens of another
                                   KV head; ABI 5                            */
@@ -204,11 +206,14 @@ size_t pkv_workspace_size(const pkv_dims* dims, int num_kv_heads, int page_size,
  * q_scale, kv_scale, sliding_win_size, kv_layout, ..., q_seq_len, mask)`).
  * `window` is sliding_win_size (0 = off).  `mask` is read only when
  * q_seq_len > 1.  `workspace` must hold dims->workspace_bytes >=
- * pkv_workspace_size(...) bytes and be 256-byte aligned.  The xqa page's
- * `semaphores` live in the workspace: on the matrix-core stream-K plan the
- * last wave to finish a piece of a (sequence, KV head) merges its partials
- * in the same launch; the latent-cache and split-grid plans merge in a second
- * kernel.  `sm_count` and `enable_pdl` have no counterpart (the CU count is
+ * pkv_workspace_size(...) bytes and be 256-byte aligned (it may be NULL
+ * when that size is 0: on the matrix-core path, when no (sequence, KV head)
+ * can span more than 17 16-token tiles and there are at most eight of them
+ * per CU, each gets one wave that streams it whole).  The xqa page's
+ * `semaphores` live in the workspace: on the matrix-core stream-K plan with
+ * short shares the last wave to finish a piece of a (sequence, KV head)
+ * merges its partials in the same launch; the other stream-K plans, the
+ * latent-cache and the split-grid plans merge in a second kernel.  `sm_count` and `enable_pdl` have no counterpart (the CU count is
  * queried).  This entry point writes the output in q's dtype with scale 1;
  * the xqa page's `rcp_out_scale` and fp8 output are pkv_options.out_fp8 and
  * pkv_options.rcp_out_scale of pkv_decode_attn_ex. */
