@@ -934,6 +934,7 @@ def test_fp8_output_needs_an_fp8_cache():
     ("d64", [1, 64, 65, 250], {}),
     ("d256", [1, 64, 65, 250], {}),
     ("wide", [(37 * i) % 257 for i in range(600)], {}),                # 600 sequences: wide schedule
+    ("win16", [3000, 10, 150, 0, 215, 1], {}),                         # 188 table pages, window 200
 ])
 def test_short_sequences_one_wave_per_unit(kind, lens, kw):
     # every unit spans at most 17 tiles (256 cached tokens, or a window that
@@ -942,7 +943,8 @@ def test_short_sequences_one_wave_per_unit(kind, lens, kw):
             "spec": SMALL["spec"],
             "d64": SMALL["gqa"].replace(head_dim_qk=64, head_dim_v=64),
             "d256": SMALL["gqa"].replace(head_dim_qk=256, head_dim_v=256),
-            "wide": SMALL["gqa"].replace(num_q_heads=8, num_kv_heads=2)}[kind]
+            "wide": SMALL["gqa"].replace(num_q_heads=8, num_kv_heads=2),
+            "win16": SMALL["gqa"].replace(page_size=16, kv_layout="NHD", window=200)}[kind]
     w = base.replace(batch=len(lens), seq_len_range=(1, max(lens)))
     print(f"[case] short units {kind} lens={lens[:8]} ({len(lens)}) {kw}", flush=True)
     inp = make(w, seed=70 + len(lens), seq_lens=lens)
