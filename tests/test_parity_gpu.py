@@ -770,13 +770,16 @@ def test_stream_k_wide_batches(kind, B):
         assert torch.equal(got[L == 0].float().cpu(), torch.zeros_like(got[L == 0].float().cpu()))
 
 
-@pytest.mark.parametrize("name", ["gqa", "spec", "mla", "fp8_unit_waves", "mla_fp8"])
+@pytest.mark.parametrize("name", ["gqa", "spec", "mla", "fp8_unit_waves", "mla_fp8", "fp8_short"])
 def test_graph_replay_matches_eager(name):
     # a captured call (workspace passed in, so nothing is allocated inside the
     # capture) replayed several times, with eager work between the replays;
-    # fp8_unit_waves: a window and two units per CU (one wave per unit)
+    # fp8_unit_waves: a window and two units per CU (one wave per unit);
+    # fp8_short: a 200-token window, one wave per short unit, no workspace
     kw = dict(num_cus=2) if name == "fp8_unit_waves" else {}
     w = MLA_SMALL if name == "mla" else SMALL[name.split("_")[0]]
+    if name == "fp8_short":
+        w = w.replace(window=200)
     if name == "mla_fp8":
         w = MLA_FP8.replace(q_dtype=torch.float8_e4m3fn)
     print(f"[case] graph replay {name}", flush=True)
@@ -818,11 +821,12 @@ def test_graph_replay_matches_eager(name):
         assert torch.equal(out, eager), f"replay {r} differs from the eager call"
 
 
-@pytest.mark.parametrize("name", ["gqa", "fp8", "mla"])
+@pytest.mark.parametrize("name", ["gqa", "fp8", "mla", "short"])
 def test_device_resident_scales(name):
     # the xqa page's q_scale / kv_scale may be tensors: one fp32 value in
-    # device memory, read when the kernels run
-    base = {"gqa": SMALL["gqa"], "fp8": SMALL["fp8"], "mla": MLA_SMALL}[name]
+    # device memory, read when the kernels run (short: one wave per unit)
+    base = {"gqa": SMALL["gqa"], "fp8": SMALL["fp8"], "mla": MLA_SMALL,
+            "short": SMALL["fp8"].replace(window=200)}[name]
     w = base.replace(q_scale=0.7, kv_scale=base.kv_scale * 1.3)
     print(f"[case] device scales {name}", flush=True)
     inp = make(w, seed=100)
@@ -882,20 +886,22 @@ def test_device_scale_arguments_checked():
 # ---------------------------------------------------------------- fp8 output (rcp_out_scale)
 
 @pytest.mark.parametrize("rcp", [1.0, 6.0])
-@pytest.mark.parametrize("mode", ["sk", "grid", "valu", "one_launch", "latent_sk", "latent_grid"])
+@pytest.mark.parametrize("mode", ["sk", "grid", "valu", "one_launch", "short", "latent_sk",
+                                  "latent_grid"])
 def test_fp8_output_with_rcp_out_scale(mode, rcp):
     # an fp8 cache may write an fp8 output holding round(out * rcp_out_scale);
     # the decoded output / rcp is within the bound plus half an E4M3 step
     # (latent: fp8 query and cache, whole units from the split kernel and cut
-    # ones from the combine)
-    w = MLA_FP8.replace(q_dtype=torch.float8_e4m3fn) if mode.startswith("latent") else SMALL["fp8"]
+    # ones from the combine; short: a 200-token window, one wave per unit)
+    w = (MLA_FP8.replace(q_dtype=torch.float8_e4m3fn) if mode.startswith("latent")
+         else SMALL["fp8"].replace(window=200) if mode == "short" else SMALL["fp8"])
     print(f"[case] fp8 output {mode} rcp={rcp}", flush=True)
     inp = make(w, seed=95)
     B = inp["q"].shape[0]
     out = torch.full((B, w.q_seq_len, w.num_q_heads, w.head_dim_v), float("nan"),
                      dtype=torch.float8_e4m3fn, device=DEV)
     kw = {"sk": {}, "grid": {"split_pages": 3}, "valu": {"path": "valu"},
-          "one_launch": {"single_launch": True, "target_ctas": 7},
+          "one_launch": {"single_launch": True, "target_ctas": 7}, "short": {},
           "latent_sk": {"target_ctas": 5}, "latent_grid": {"split_pages": 3}}[mode]
     pkv.decode_attn(inp["q"], inp["k_cache"], inp["v_cache"], inp["page_table"], inp["seq_lens"],
                     out, num_kv_heads=w.num_kv_heads, page_size=w.page_size, sinks=inp["sinks"],

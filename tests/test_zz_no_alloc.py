@@ -69,6 +69,8 @@ CASES = {
     "fp8_unit_waves": dict(num_cus=2),
     # fp8 query and latent cache (64-token tiles), four workgroups
     "mla_fp8": dict(target_ctas=4),
+    # at most 256 tokens a sequence: one wave per unit, no scratch at all
+    "gqa_short": dict(),
 }
 
 
@@ -81,6 +83,8 @@ def test_noalloc_matches_workspace_entry_point(case):
     if case == "mla_fp8":
         w1 = w1.replace(q_dtype=torch.float8_e4m3fn, kv_dtype=torch.float8_e4m3fn, kv_scale=0.05,
                         kv_gen_scale=1.0 / 0.05)
+    if case == "gqa_short":
+        w1 = w1.replace(seq_len_range=(1, 256))
     lo, hi = w1.seq_len_range
     w2 = w1.replace(batch=max(1, w1.batch - 2), seq_len_range=(lo, max(lo, hi // 3)))
     for step, (w, seed) in enumerate(((w1, 201), (w2, 202))):
