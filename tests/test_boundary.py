@@ -151,6 +151,18 @@ def test_plan_one_wave_per_short_unit():
     mla = plan(batch=2, num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
                pages_per_seq=4, page_size=64)
     assert mla["workspace_bytes"] > 0                      # the latent path keeps stream-K
+    # the edges: a window reaching 256 tokens (window + q_seq_len - 1) or one
+    # more; exactly eight units per CU or one more; an explicit merge choice;
+    # the vector path
+    assert plan(batch=8, pages_per_seq=128, page_size=64, window=253, q_seq_len=4)["workspace_bytes"] == 0
+    assert plan(batch=8, pages_per_seq=128, page_size=64, window=254, q_seq_len=4)["workspace_bytes"] > 0
+    assert plan(batch=256, pages_per_seq=4, page_size=64, num_cus=256)["workspace_bytes"] == 0  # 2048 units
+    assert plan(batch=257, pages_per_seq=4, page_size=64, num_cus=256)["workspace_bytes"] > 0
+    for merge in (True, False):
+        p = plan(batch=64, pages_per_seq=4, page_size=64, single_launch=merge)
+        assert p["workspace_bytes"] > 0 and p["single_launch"] == (1 if merge else 0)
+    valu = plan(batch=2, pages_per_seq=4, page_size=64, path="valu")   # the split grid
+    assert valu["path"] == pkv.PATH_VALU and valu["split_pages"] == 4 and valu["single_launch"] == 0
 
 
 def test_plan_one_wave_per_windowed_unit():
